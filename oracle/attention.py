@@ -1,0 +1,233 @@
+"""Plain CPU oracle for exact scaled-dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module:
+only the test-suite, the package smoke check and the benchmark's CPU-baseline
+leg use it.  It shares no code, constants or helpers with the HIP kernels.
+
+Everything is computed in float64 with NumPy, materialising the full score
+matrix S and the probability matrix P for each head, exactly as standard
+attention is defined; there is no online softmax, no tiling of the key axis
+and no reordering.  The only concession to memory is that query rows are
+processed in chunks of whole rows (every chunk still sees all keys of its
+rows), which leaves each row's softmax the textbook one.
+
+Sources (cited by page title and section):
+  [FA2] "FlashAttention-2: Faster Attention with Better Parallelism and Work
+        Partitioning (ICLR 2024)", wiki summary, sections "Problem and
+        motivation" (standard attention materialises S = QK^T and
+        P = softmax(S)) and "Core method" items 1 (only the logsumexp
+        L = m + log(l) is kept for the backward), 2 (causal mask: keys with a
+        column index above the row index are excluded) and 4 (MQA/GQA: K/V
+        heads are shared by index mapping; the backward sums dK, dV over the
+        implicitly replicated heads).
+  The backward formulas (recompute P from the logsumexp, dV = P^T dO,
+  dP = dO V^T, dS = P o (dP - D) with D = rowsum(dO o O), dK = dS^T Q,
+  dQ = dS K) are the chain rule of the forward definition.  Readings taken
+  where the pages are silent:
+    * dS is the gradient with respect to the *scaled* scores s = scale*q.k,
+      so dQ = scale * dS K and dK = scale * dS^T Q (the true gradient; pinned
+      by finite differences in the tests).
+    * the logsumexp is the natural log of sum_j exp(scale * q_i . k_j).
+    * causal masking is top-left aligned: key j is visible to query i iff
+      j <= i (queries and keys always have the same length here).
+    * GQA maps query head h to key/value head h // (Hq // Hkv).
+
+Layouts (token-major, as in the library): dense Q/O/dO/dQ are [B, N, Hq, d],
+K/V/dK/dV are [B, N, Hkv, d], the logsumexp is [B, Hq, N]; packed
+variable-length tensors are [T, H, d] with cu_seqlens offsets and a
+logsumexp of shape [Hq, T].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ROW_CHUNK = 2048
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _group(hq: int, hkv: int) -> int:
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError(f"Hq={hq} must be a positive multiple of Hkv={hkv}")
+    return hq // hkv
+
+
+def head_scores(qh, kh, scale: float, causal: bool, row0: int = 0) -> np.ndarray:
+    """Scaled score rows S[i, j] = scale * q_i . k_j for queries row0.. of one head.
+
+    Causal: S[i, j] = -inf where key j > query i ([FA2] "Core method" 2).
+    """
+    s = scale * (qh @ kh.T)
+    if causal:
+        rows = np.arange(row0, row0 + qh.shape[0])[:, None]
+        cols = np.arange(kh.shape[0])[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    return s
+
+
+def head_probs(qh, kh, scale: float, causal: bool, row0: int = 0):
+    """Row softmax of the scores and its natural-log normaliser.
+
+    Returns (P, lse) with lse_i = ln sum_j exp(S_ij), computed stably as
+    m_i + ln sum_j exp(S_ij - m_i), and P = exp(S - lse)
+    ([FA2] "Problem and motivation"; "Core method" 1 for L = m + log l).
+    """
+    s = head_scores(qh, kh, scale, causal, row0)
+    m = s.max(axis=1)
+    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    p = np.exp(s - lse[:, None])
+    return p, lse
+
+
+def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
+    """Full probability tensor P[b, h, i, j] (small inputs only; used by the pins)."""
+    q, k = _f64(q), _f64(k)
+    B, N, Hq, _ = q.shape
+    G = _group(Hq, k.shape[2])
+    out = np.empty((B, Hq, N, k.shape[1]))
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h], _ = head_probs(q[b, :, h], k[b, :, h // G], scale, causal)
+    return out
+
+
+def _head_forward(qh, kh, vh, scale, causal, row_chunk):
+    n = qh.shape[0]
+    o = np.empty((n, vh.shape[1]))
+    lse = np.empty(n)
+    for r0 in range(0, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        p, lse[r0:r1] = head_probs(qh[r0:r1], kh, scale, causal, r0)
+        o[r0:r1] = p @ vh
+    return o, lse
+
+
+def _head_backward(qh, kh, vh, doh, scale, causal, row_chunk):
+    """Gradients of one query head against its key/value head.
+
+    Per chunk of whole query rows: recompute P from the definition, O = P V,
+    D = rowsum(dO o O), dV += P^T dO, dP = dO V^T, dS = P o (dP - D),
+    dQ = scale dS K, dK += scale dS^T Q.
+    """
+    n = qh.shape[0]
+    dq = np.empty_like(qh)
+    dk = np.zeros_like(kh)
+    dv = np.zeros_like(vh)
+    for r0 in range(0, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        q_c, do_c = qh[r0:r1], doh[r0:r1]
+        p, _ = head_probs(q_c, kh, scale, causal, r0)
+        o_c = p @ vh
+        d_c = (do_c * o_c).sum(axis=1)
+        dv += p.T @ do_c
+        dp = do_c @ vh.T
+        ds = p * (dp - d_c[:, None])
+        dq[r0:r1] = scale * (ds @ kh)
+        dk += scale * (ds.T @ q_c)
+    return dq, dk, dv
+
+
+def attention_forward(q, k, v, scale: float, causal: bool, row_chunk: int = ROW_CHUNK):
+    """Dense forward.  q [B,N,Hq,d], k/v [B,N,Hkv,d] -> (o [B,N,Hq,d], lse [B,Hq,N])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, Hq, d = q.shape
+    G = _group(Hq, k.shape[2])
+    o = np.empty((B, N, Hq, v.shape[3]))
+    lse = np.empty((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            o[b, :, h], lse[b, h] = _head_forward(q[b, :, h], k[b, :, g], v[b, :, g],
+                                                  scale, causal, row_chunk)
+    return o, lse
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool, row_chunk: int = ROW_CHUNK):
+    """Dense backward -> (dq [B,N,Hq,d], dk [B,N,Hkv,d], dv [B,N,Hkv,d]).
+
+    dK and dV of a key/value head are summed over the query heads of its group
+    ([FA2] "Core method" 4).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = _group(Hq, Hkv)
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            dqh, dkh, dvh = _head_backward(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h],
+                                           scale, causal, row_chunk)
+            dq[b, :, h] = dqh
+            dk[b, :, g] += dkh
+            dv[b, :, g] += dvh
+    return dq, dk, dv
+
+
+def _check_cu(cu, total):
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    return cu
+
+
+def varlen_forward(q, k, v, cu_seqlens, scale: float, causal: bool, row_chunk: int = ROW_CHUNK):
+    """Packed variable-length forward: each sequence is attention on its own slice.
+
+    q [T,Hq,d], k/v [T,Hkv,d] -> (o [T,Hq,d], lse [Hq,T]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = _check_cu(cu_seqlens, q.shape[0])
+    o = np.zeros_like(q)
+    lse = np.zeros((q.shape[1], q.shape[0]))
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        o_s, lse_s = attention_forward(q[None, a:e], k[None, a:e], v[None, a:e],
+                                       scale, causal, row_chunk)
+        o[a:e] = o_s[0]
+        lse[:, a:e] = lse_s[0]
+    return o, lse
+
+
+def varlen_backward(q, k, v, do, cu_seqlens, scale: float, causal: bool,
+                    row_chunk: int = ROW_CHUNK):
+    """Packed variable-length backward -> (dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d])."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    cu = _check_cu(cu_seqlens, q.shape[0])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        g = attention_backward(q[None, a:e], k[None, a:e], v[None, a:e], do[None, a:e],
+                               scale, causal, row_chunk)
+        dq[a:e], dk[a:e], dv[a:e] = g[0][0], g[1][0], g[2][0]
+    return dq, dk, dv
+
+
+def head_forward_backward(qh, kh, vh, doh, scale: float, causal: bool,
+                          row_chunk: int = ROW_CHUNK):
+    """One query head end to end (used to time the oracle on a sample of heads).
+
+    Returns (o, lse, dq, dk, dv) for that head.
+    """
+    qh, kh, vh, doh = _f64(qh), _f64(kh), _f64(vh), _f64(doh)
+    o, lse = _head_forward(qh, kh, vh, scale, causal, row_chunk)
+    dq, dk, dv = _head_backward(qh, kh, vh, doh, scale, causal, row_chunk)
+    return o, lse, dq, dk, dv
+
+
+def attention_flops(B: int, N: int, Hq: int, d: int, causal: bool) -> tuple[float, float]:
+    """Algorithmic FLOP convention: forward 4 B Hq N^2 d (halved when causal),
+    backward 2.5x the forward ([FA2] "Critical analysis": causal FLOPs halved)."""
+    f = 4.0 * B * Hq * N * N * d * (0.5 if causal else 1.0)
+    return f, 2.5 * f
