@@ -1,0 +1,445 @@
+// fa_api.hip -- C ABI of the library: argument validation, workspace layout,
+// device check and launch sequencing.  Declarations and the contract of every
+// entry point are in include/fa.h.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+using fa::BwdParams;
+using fa::FwdParams;
+
+constexpr int kAbiVersion = 1;
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// device check (gfx950 only), cached per device
+
+struct DevInfo {
+  bool gfx950 = false;
+  int cus = 0;
+  std::string arch;
+};
+
+std::mutex g_dev_mu;
+std::unordered_map<int, DevInfo> g_dev;
+
+int check_device(std::string* why) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *why = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return FA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      *why = std::string("hipGetDeviceProperties: ") + hipGetErrorString(e);
+      return FA_ERR_HIP;
+    }
+    DevInfo info;
+    info.arch = prop.gcnArchName;
+    info.gfx950 = info.arch.rfind("gfx950", 0) == 0;
+    info.cus = prop.multiProcessorCount;
+    it = g_dev.emplace(dev, info).first;
+  }
+  if (!it->second.gfx950) {
+    *why = "device " + std::to_string(dev) + " is " + it->second.arch + ", not gfx950";
+    return FA_ERR_DEVICE;
+  }
+  return FA_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+// Ablation switch for the tile order: FA_SCHED=natural disables longest-first
+// and XCD grouping (read on every call; results never depend on it).
+int sched_mode() {
+  const char* s = std::getenv("FA_SCHED");
+  return (s && std::strcmp(s, "natural") == 0) ? 1 : 0;
+}
+
+// Bound of a deterministic-mode wait, in ticks of the 100 MHz real-time clock.
+uint32_t spin_limit() {
+  const int v = env_int("FA_DET_SPIN_TICKS", 0);
+  return v > 0 ? (uint32_t)v : 200000000u;  // 2 s
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(FA_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(FA_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return FA_OK;
+}
+
+int check_dims(long tokens, int Hq, int Hkv, int d, int causal, float scale) {
+  if (tokens <= 0) return fail(FA_ERR_INVALID_ARG, "sequence length / token count must be positive");
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive");
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(FA_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (tokens * (long)Hq * d >= (1L << 31) * 16L)
+    return fail(FA_ERR_UNSUPPORTED, "tensor too large");
+  if (tokens > (1L << 30)) return fail(FA_ERR_UNSUPPORTED, "too many tokens");
+  return FA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+
+struct FwdLayout {
+  size_t hdr = 0, tiles = 0, total = 0;
+  int max_tiles = 0;
+};
+
+FwdLayout fwd_layout(bool varlen, int nseq, long T) {
+  FwdLayout l;
+  if (!varlen) return l;
+  l.max_tiles = (int)(T / fa::fwd_tile_rows() + nseq);
+  l.hdr = 0;
+  l.tiles = align_up(fa::kHdrWords * 4);
+  l.total = l.tiles + align_up((size_t)l.max_tiles * 2 * 4);
+  return l;
+}
+
+struct BwdLayout {
+  size_t hdr = 0, dvec = 0, dq_acc = 0, sem = 0, tiles = 0, dk_part = 0, dv_part = 0, total = 0;
+  long sem_count = 0;
+  int sem_slots = 0;  // varlen: per head
+  int max_tiles = 0;
+  int S = 1;
+};
+
+// Query-head subgroups per key/value head: split a group when there are too
+// few (sequence, key/value head, key tile) work items to fill the GPU.  The
+// choice depends only on the shapes, so it is the same for the size query and
+// the call.
+int choose_split(long units, int G) {
+  const int env = env_int("FA_BWD_SPLIT", 0);
+  if (env > 0 && G % env == 0) return env;
+  for (int S = 1; S <= G; ++S)
+    if (G % S == 0 && units * S >= 1024) return S;
+  return G;
+}
+
+BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, int Hq, int Hkv, int d,
+                     int deterministic) {
+  BwdLayout l;
+  const int G = Hq / Hkv;
+  long units;
+  if (varlen) {
+    l.max_tiles = (int)(T / fa::kBwdBC + nseq);
+    units = (long)Hkv * (T / fa::kBwdBC + 1);
+  } else {
+    units = (long)B * Hkv * cdiv(N, fa::kBwdBC);
+  }
+  l.S = choose_split(units, G);
+  size_t off = align_up(fa::kHdrWords * 4);
+  l.dvec = off;
+  off += align_up((size_t)T * Hq * 4);
+  l.dq_acc = off;
+  off += align_up((size_t)T * Hq * d * 4);
+  if (deterministic) {
+    if (varlen) {
+      l.sem_slots = (int)(T / fa::kBwdBQ + nseq + 1);
+      l.sem_count = (long)Hq * l.sem_slots;
+    } else {
+      l.sem_count = (long)B * Hq * cdiv(N, fa::kBwdBQ);
+    }
+  }
+  l.sem = off;
+  off += align_up((size_t)l.sem_count * 4);
+  if (varlen) {
+    l.tiles = off;
+    off += align_up((size_t)l.max_tiles * 2 * 4);
+  }
+  if (l.S > 1) {
+    l.dk_part = off;
+    off += align_up((size_t)l.S * T * Hkv * d * 4);
+    l.dv_part = off;
+    off += align_up((size_t)l.S * T * Hkv * d * 4);
+  }
+  l.total = off;
+  return l;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// shared implementations of dense and varlen calls
+
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, int B,
+            int N, const int32_t* cu, int nseq, long T, int Hq, int Hkv, int d, float scale,
+            int causal, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
+    return st;
+  if (varlen && (st = check_ptr(cu, "cu_seqlens"))) return st;
+  if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
+  const FwdLayout lay = fwd_layout(varlen, nseq, T);
+  if (ws_bytes < lay.total || (lay.total > 0 && !ws))
+    return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*fwd_workspace_size()");
+  if (lay.total > 0 && (st = check_ptr(ws, "ws"))) return st;
+  std::string why;
+  if ((st = check_device(&why))) return fail(st, why);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FwdParams p{};
+  p.q = static_cast<const fa::bf16*>(q);
+  p.k = static_cast<const fa::bf16*>(k);
+  p.v = static_cast<const fa::bf16*>(v);
+  p.o = static_cast<fa::bf16*>(o);
+  p.lse = lse;
+  p.B = B;
+  p.N = N;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.T = (int)T;
+  p.sched = sched_mode();
+  p.c = scale * fa::kLog2e;
+  const int br = fa::fwd_tile_rows();
+  long grid;
+  hipError_t e;
+  if (varlen) {
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, lay.hdr));
+    int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
+    e = fa::launch_sched(cu, nseq, (int)T, br, 0, causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ,
+                         tiles, lay.max_tiles, hdr, s);
+    if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+    p.cu_seqlens = cu;
+    p.tiles = tiles;
+    p.hdr = hdr;
+    grid = (long)lay.max_tiles * Hq;
+  } else {
+    p.nq = (int)cdiv(N, br);
+    grid = (long)p.nq * B * Hq;
+  }
+  if (grid <= 0) return FA_OK;
+  if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  e = fa::launch_fwd(p, d, causal != 0, varlen, (int)grid, s);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return FA_OK;
+}
+
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, bool varlen, int B, int N,
+            const int32_t* cu, int nseq, long T, int Hq, int Hkv, int d, float scale, int causal,
+            int deterministic, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(lse, "lse")) ||
+      (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
+    return st;
+  if (varlen && (st = check_ptr(cu, "cu_seqlens"))) return st;
+  if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
+  if (deterministic != 0 && deterministic != 1)
+    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0 or 1");
+  const BwdLayout lay = bwd_layout(varlen, B, N, nseq, T, Hq, Hkv, d, deterministic);
+  if (!ws || ws_bytes < lay.total)
+    return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*bwd_workspace_size()");
+  if ((st = check_ptr(ws, "ws"))) return st;
+  std::string why;
+  if ((st = check_device(&why))) return fail(st, why);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, 0));
+  float* dvec = reinterpret_cast<float*>(at(ws, lay.dvec));
+  float* dq_acc = reinterpret_cast<float*>(at(ws, lay.dq_acc));
+  int* sem = reinterpret_cast<int*>(at(ws, lay.sem));
+  hipError_t e = fa::launch_bwd_pre(static_cast<const fa::bf16*>(o),
+                                    static_cast<const fa::bf16*>(dout), dvec, dq_acc, sem,
+                                    lay.sem_count, hdr, (int)(T * Hq), Hq, d, varlen, N, (int)T, s);
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+
+  BwdParams p{};
+  p.q = static_cast<const fa::bf16*>(q);
+  p.k = static_cast<const fa::bf16*>(k);
+  p.v = static_cast<const fa::bf16*>(v);
+  p.dout = static_cast<const fa::bf16*>(dout);
+  p.lse = lse;
+  p.dvec = dvec;
+  p.dq_acc = dq_acc;
+  p.dk = static_cast<fa::bf16*>(dk);
+  p.dv = static_cast<fa::bf16*>(dv);
+  p.dk_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dk_part)) : nullptr;
+  p.dv_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dv_part)) : nullptr;
+  p.sem = sem;
+  p.hdr = hdr;
+  p.B = B;
+  p.N = N;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.S = lay.S;
+  p.T = (int)T;
+  p.sem_slots = lay.sem_slots;
+  p.sched = sched_mode();
+  p.c = scale * fa::kLog2e;
+  p.scale = scale;
+  p.spin_limit = spin_limit();
+  long grid;
+  if (varlen) {
+    int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
+    e = fa::launch_sched(cu, nseq, (int)T, fa::kBwdBC, deterministic ? 2 : 1, causal != 0,
+                         fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles, hdr, s);
+    if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+    p.cu_seqlens = cu;
+    p.tiles = tiles;
+    grid = (long)lay.max_tiles * Hkv * lay.S;
+  } else {
+    p.nkv = (int)cdiv(N, fa::kBwdBC);
+    p.nq = (int)cdiv(N, fa::kBwdBQ);
+    grid = (long)B * Hkv * lay.S * p.nkv;
+  }
+  if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (grid > 0) {
+    e = fa::launch_bwd(p, d, causal != 0, varlen, deterministic != 0, (int)grid, s);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+  }
+  e = fa::launch_bwd_post(dq_acc, static_cast<fa::bf16*>(dq), T * Hq * d, scale, p.dk_part,
+                          p.dv_part, static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
+                          T * Hkv * d, lay.S, s);
+  if (e != hipSuccess) return hip_fail(e, "backward post launch");
+  return FA_OK;
+}
+
+bool dense_ok(int B, int N) { return B > 0 && N > 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return kAbiVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_DEVICE: return "FA_ERR_DEVICE";
+    case FA_ERR_DEVICE_REPORTED: return "FA_ERR_DEVICE_REPORTED";
+    default: return "FA_ERR_UNKNOWN";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+size_t fa_fwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal) {
+  (void)B; (void)N; (void)Hq; (void)Hkv; (void)d; (void)causal;
+  return 0;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N, int Hq,
+           int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
+           void* stream) {
+  if (!dense_ok(B, N)) return fail(FA_ERR_INVALID_ARG, "B and N must be positive");
+  return run_fwd(q, k, v, o, lse, false, B, N, nullptr, 0, (long)B * N, Hq, Hkv, d,
+                 softmax_scale, causal, ws, ws_bytes, stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
+                             int deterministic) {
+  (void)causal;
+  if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+  return bwd_layout(false, B, N, 0, (long)B * N, Hq, Hkv, d, deterministic != 0).total;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int N, int Hq, int Hkv, int d,
+           float softmax_scale, int causal, int deterministic, void* ws, size_t ws_bytes,
+           void* stream) {
+  if (!dense_ok(B, N)) return fail(FA_ERR_INVALID_ARG, "B and N must be positive");
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, false, B, N, nullptr, 0, (long)B * N, Hq, Hkv,
+                 d, softmax_scale, causal, deterministic, ws, ws_bytes, stream);
+}
+
+size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
+                                    int causal) {
+  (void)Hq; (void)Hkv; (void)d; (void)causal;
+  if (nseq <= 0 || total_tokens <= 0) return 0;
+  return fwd_layout(true, nseq, total_tokens).total;
+}
+
+int fa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen, int Hq,
+                  int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
+  if (max_seqlen < 0) return fail(FA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
+  return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens, nseq, total_tokens, Hq, Hkv, d,
+                 softmax_scale, causal, ws, ws_bytes, stream);
+}
+
+size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
+                                    int causal, int deterministic) {
+  (void)causal;
+  if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+  return bwd_layout(true, 0, 0, nseq, total_tokens, Hq, Hkv, d, deterministic != 0).total;
+}
+
+int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                  int nseq, int total_tokens, int max_seqlen, int Hq, int Hkv, int d,
+                  float softmax_scale, int causal, int deterministic, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
+  if (max_seqlen < 0) return fail(FA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, true, 1, 0, cu_seqlens, nseq, total_tokens,
+                 Hq, Hkv, d, softmax_scale, causal, deterministic, ws, ws_bytes, stream);
+}
+
+int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* bits) {
+  if (!ws) return fail(FA_ERR_INVALID_ARG, "ws is NULL");
+  if (ws_bytes < fa::kHdrWords * 4) return fail(FA_ERR_WORKSPACE, "workspace has no header");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t w = 0;
+  e = hipMemcpy(&w, ws, sizeof(w), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  if (bits) *bits = w;
+  if (w == 0) return FA_OK;
+  std::string msg = "device reported:";
+  if (w & FA_DEVERR_BAD_CU_SEQLENS) msg += " bad cu_seqlens;";
+  if (w & FA_DEVERR_WAIT_TIMEOUT) msg += " deterministic wait timed out;";
+  if (w & FA_DEVERR_TILE_OVERFLOW) msg += " tile list overflow;";
+  return fail(FA_ERR_DEVICE_REPORTED, msg);
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// fa_common.h -- device-side building blocks shared by the gfx950 attention kernels.
+//
+// Everything here is written for CDNA4 (gfx950) wave64 execution:
+//  * v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] * B[16x32], bf16 in, fp32 out.
+//    Operand A: lane l holds A[m = l%32][k = 8*(l/32) + j], j = 0..7 (8 bf16).
+//    Operand B: lane l holds B[k = 8*(l/32) + j][n = l%32].
+//    Result C : lane l holds C[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32], r = 0..15.
+//  * A result fragment read along its rows therefore gives, per 16-row chunk c
+//    (registers 8c..8c+7), exactly the 8 rows that the next product needs as
+//    its k-slice in lane half l/32, in the order
+//        row(c, half, j) = 16*(c%2) + 8*(j/4) + 4*half + j%4   (within 32 rows).
+//    Every second operand that pairs with such a register fragment is stored in
+//    LDS with its k axis permuted the same way (kperm16 below), so the
+//    fragment is used in place with no cross-lane shuffle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Device error word bits (mirrors include/fa.h).
+constexpr uint32_t kErrBadCu = 1u;
+constexpr uint32_t kErrWaitTimeout = 2u;
+constexpr uint32_t kErrTileOverflow = 4u;
+
+// Workspace header (in 32-bit words) used by the varlen scheduler and the backward.
+constexpr int kHdrErr = 0;       // error bits (atomic OR)
+constexpr int kHdrTicket = 1;    // deterministic backward work-item ticket
+constexpr int kHdrCount = 2;     // number of valid entries in the tile list
+constexpr int kHdrWords = 64;    // 256 bytes
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 b) { return __builtin_bit_cast(u32x4, b); }
+
+// Pack 8 fp32 values (round to nearest even) into one MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3,
+                                        float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+  return r;
+}
+
+// Two fp32 values rounded to bf16 (nearest even) packed into one 32-bit word.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(unsigned short, (bf16)a);
+  const uint32_t hi = __builtin_bit_cast(unsigned short, (bf16)b);
+  return lo | (hi << 16);
+}
+
+// Registers 8c..8c+7 of a result fragment as one operand.
+__device__ __forceinline__ bf16x8 frag_rows(const f32x16& x, int c) {
+  return pack8(x[8 * c + 0], x[8 * c + 1], x[8 * c + 2], x[8 * c + 3],
+               x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]);
+}
+
+// Position, inside a 64-element row, at which element kk (0..63) of the permuted
+// k axis is stored so that a 16-byte read at 16*c2 + 8*half returns the rows a
+// result fragment holds in registers 8*(c2%2).. of lane half `half` (see top).
+__device__ __forceinline__ int kperm16(int kk) {
+  const int r16 = kk & 15;
+  return (kk & ~15) + ((r16 >> 2) & 1) * 8 + (r16 >> 3) * 4 + (r16 & 3);
+}
+
+// Bitwise pack of two bf16 lanes of two 32-bit words (select low or high halves).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);  // {a.lo, b.lo}
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // {a.hi, b.hi}
+}
+
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld_lds16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_lds16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st_lds8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  // lanes l and l^32 hold the two halves of the same query row
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposed 4x8 store: rows r0..r3 each hold 8 bf16 (a 16-byte chunk of a
+// row-major tile, columns c..c+7).  Writes, for every column, the 4 values as
+// one 8-byte word into a column-major tile at (column row stride `stride`
+// bytes, byte offset `pos_bytes` inside each column row).
+__device__ __forceinline__ void store_transposed_4x8(char* base, int stride, int pos_bytes,
+                                                     const u32x4& r0, const u32x4& r1,
+                                                     const u32x4& r2, const u32x4& r3) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32x2 lo, hi;
+    lo[0] = pack_lo(r0[w], r1[w]);
+    lo[1] = pack_lo(r2[w], r3[w]);
+    hi[0] = pack_hi(r0[w], r1[w]);
+    hi[1] = pack_hi(r2[w], r3[w]);
+    st_lds8(base + (2 * w) * stride + pos_bytes, lo);
+    st_lds8(base + (2 * w + 1) * stride + pos_bytes, hi);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks (plain structs passed by value).
+
+struct FwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  const int* cu_seqlens;  // varlen only
+  const int* tiles;       // varlen only: (sequence, q-tile) pairs in schedule order
+  const uint32_t* hdr;    // varlen only: workspace header (error word, tile count)
+  int B, N, Hq, Hkv, G;   // dense: N is the sequence length
+  int T;                  // total tokens (varlen LSE layout [Hq, T])
+  int nq;                 // dense: number of query tiles per sequence
+  int sched;              // 0: longest-first, XCD-grouped; 1: natural order
+  float c;                // softmax_scale * log2(e)
+};
+
+struct BwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* dout;
+  const float* lse;
+  const float* dvec;      // D = rowsum(dO o O), laid out like lse
+  float* dq_acc;          // [T, Hq, d] fp32
+  bf16* dk;
+  bf16* dv;
+  float* dk_part;         // [S, T, Hkv, d] fp32 when S > 1
+  float* dv_part;
+  int* sem;               // dQ tile semaphores (deterministic mode)
+  uint32_t* hdr;          // workspace header
+  const int* cu_seqlens;  // varlen only
+  const int* tiles;       // varlen only: (sequence, kv-tile) pairs in schedule order
+  int B, N, Hq, Hkv, G, S;
+  int T;
+  int nkv;                // dense: number of key tiles per sequence
+  int nq;                 // dense: number of query tiles per sequence
+  int sem_slots;          // varlen: semaphore slots per head
+  int sched;
+  float c;                // softmax_scale * log2(e)
+  float scale;
+  uint32_t spin_limit;    // deterministic wait bound (polls)
+};
+
+}  // namespace fa

@@ -1,0 +1,324 @@
+// fa_fwd.hip -- fused attention forward for gfx950.
+//
+// Method ([FA2] "Core method" 1-3, [FA4N] co-design list):
+//  * one workgroup per (sequence, query head, query tile of BR = 32*NW rows);
+//    the tiles are independent, so the output never depends on launch order;
+//  * split-Q: wave w owns query rows 32w..32w+31 of the tile and sees every
+//    key/value tile, so no reduction between waves is ever needed;
+//  * K/V tiles of 64 keys stream through LDS, double buffered: the global
+//    loads of tile j+1 are in flight while tile j is computed;
+//  * the score tile is computed transposed, S^T = K Q^T, so each lane holds one
+//    query column: the row max and row sum are in-lane plus one exchange with
+//    lane l^32;
+//  * online softmax in base 2 with conditional rescaling: a stale reference max
+//    is kept and the accumulator is rescaled only when a row max grows by more
+//    than kTau (log2 units), decided per wave; probabilities therefore stay
+//    below 2^kTau and the result is unchanged;
+//  * the unscaled output accumulator O^T += V^T P^T stays in registers and is
+//    divided by the row sum once at the end; only LSE = ln(sum exp) is saved;
+//  * causal: key tiles wholly above a wave's rows are skipped, the mask is
+//    applied only on tiles that straddle the diagonal or the sequence end.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBC = 64;        // keys per K/V tile
+constexpr float kTau = 8.0f;   // rescale threshold (log2 units): p <= 2^8
+
+template <int D>
+struct FwdTile {
+  static constexpr int kStride = D * 2 + 16;   // bytes per key row of the K tile
+  static constexpr int vStride = kBC * 2 + 16; // bytes per d row of the V^T tile
+  static constexpr int kBytes = kBC * kStride;
+  static constexpr int vBytes = D * vStride;
+  static constexpr int bufBytes = kBytes + vBytes;
+};
+
+struct WorkItem {
+  int seq_start;  // first token of the sequence
+  int seq_len;
+  int b;          // batch index (dense) or sequence index (varlen)
+  int h;          // query head
+  int qtile;
+  bool valid;
+};
+
+template <bool CAUSAL, bool VARLEN, int BR>
+__device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
+  WorkItem w;
+  const int t = blockIdx.x;
+  if (VARLEN) {
+    const int e = t / p.Hq;
+    w.h = t - e * p.Hq;
+    const int count = (int)p.hdr[kHdrCount];
+    w.valid = e < count && (p.hdr[kHdrErr] & kErrBadCu) == 0;
+    if (!w.valid) return w;
+    w.b = p.tiles[2 * e];
+    w.qtile = p.tiles[2 * e + 1];
+    w.seq_start = p.cu_seqlens[w.b];
+    w.seq_len = p.cu_seqlens[w.b + 1] - w.seq_start;
+  } else {
+    const int BH = p.B * p.Hq;
+    int i, bh;
+    if (p.sched == 0 && (BH & 7) == 0) {
+      // consecutive workgroups go to different XCDs (round robin over 8): give
+      // each XCD a contiguous block of heads so the query heads of one
+      // key/value head share that XCD's L2; inside it, most expensive first
+      const int x = t & 7, r = t >> 3, hx = BH >> 3;
+      const int ii = r / hx;
+      bh = x * hx + (r - ii * hx);
+      i = CAUSAL ? (p.nq - 1 - ii) : ii;
+    } else if (p.sched == 0) {
+      const int ii = t / BH;
+      bh = t - ii * BH;
+      i = CAUSAL ? (p.nq - 1 - ii) : ii;
+    } else {
+      bh = t / p.nq;
+      i = t - bh * p.nq;
+    }
+    w.b = bh / p.Hq;
+    w.h = bh - w.b * p.Hq;
+    w.qtile = i;
+    w.seq_start = w.b * p.N;
+    w.seq_len = p.N;
+    w.valid = true;
+  }
+  return w;
+}
+
+template <int D, int NW, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;
+  using L = FwdTile<D>;
+  constexpr int KCH = kBC * D / 8;     // 16-byte chunks in a K tile
+  constexpr int KIT = (KCH + NT - 1) / NT;
+  constexpr int VBL = (kBC / 4) * (D / 8);  // 4-key x 8-d blocks in a V tile
+  constexpr int VIT = (VBL + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::bufBytes];
+
+  const WorkItem wi = fwd_work_item<CAUSAL, VARLEN, BR>(p);
+  if (!wi.valid) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  const int q0 = wi.qtile * BR;
+  if (q0 >= wi.seq_len) return;
+  const int hkv = wi.h / p.G;
+  const long q_row = (long)p.Hq * D;   // elements between consecutive tokens
+  const long kv_row = (long)p.Hkv * D;
+  const bf16* qbase = p.q + (long)wi.seq_start * q_row + (long)wi.h * D;
+  const bf16* kbase = p.k + (long)wi.seq_start * kv_row + (long)hkv * D;
+  const bf16* vbase = p.v + (long)wi.seq_start * kv_row + (long)hkv * D;
+
+  // ---- this lane's query and its Q fragments (operand B of S^T = K Q^T)
+  const int wq0 = q0 + wave * 32;
+  const int qi = wq0 + l32;
+  const bool q_ok = qi < wi.seq_len;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (q_ok) u = ld_global16(qbase + (long)qi * q_row + dc * 16 + half * 8);
+    qf[dc] = as_bf16x8(u);
+  }
+
+  const int kv_end = CAUSAL ? min(wi.seq_len, q0 + BR) : wi.seq_len;
+  const int nt = (kv_end + kBC - 1) / kBC;
+
+  // ---- global -> register staging of one K/V tile
+  u32x4 kst[KIT];
+  u32x4 vst[VIT][4];
+  auto load_tile = [&](int j) {
+    const int key0 = j * kBC;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int c = tid + it * NT;
+      const int row = c / (D / 8), col = c % (D / 8);
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (c < KCH && key0 + row < wi.seq_len)
+        u = ld_global16(kbase + (long)(key0 + row) * kv_row + col * 8);
+      kst[it] = u;
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int c = tid + it * NT;
+      const int a = c & 15, bcol = c >> 4;  // keys 4a..4a+3, d 8*bcol..+7
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x4 u = {0u, 0u, 0u, 0u};
+        if (c < VBL && key0 + 4 * a + r < wi.seq_len)
+          u = ld_global16(vbase + (long)(key0 + 4 * a + r) * kv_row + bcol * 8);
+        vst[it][r] = u;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kt = smem + buf * L::bufBytes;
+    char* vt = kt + L::kBytes;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int c = tid + it * NT;
+      if (c < KCH) {
+        const int row = c / (D / 8), col = c % (D / 8);
+        st_lds16(kt + row * L::kStride + col * 16, kst[it]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int c = tid + it * NT;
+      if (c < VBL) {
+        const int a = c & 15, bcol = c >> 4;
+        const int pos = kperm16(4 * a);  // 4 consecutive keys land contiguously
+        store_transposed_4x8(vt + (bcol * 8) * L::vStride, L::vStride, pos * 2,
+                             vst[it][0], vst[it][1], vst[it][2], vst[it][3]);
+      }
+    }
+  };
+
+  // ---- running softmax state (per lane = per query; both lane halves agree)
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_ref = -INFINITY;  // reference max in scaled log2 units
+  float lsum = 0.f;         // this lane half's partial row sum
+
+  if (nt > 0) load_tile(0);
+  for (int j = 0; j < nt; ++j) {
+    const int buf = j & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (j + 1 < nt) load_tile(j + 1);
+
+    const int key0 = j * kBC;
+    const bool active = !CAUSAL || key0 <= wq0 + 31;
+    if (active) {
+      const char* kt = smem + buf * L::bufBytes;
+      const char* vt = kt + L::kBytes;
+      // S^T = K Q^T for two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = as_bf16x8(ld_lds16(kt + (kb * 32 + l32) * L::kStride + dc * 32 + half * 16));
+          s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
+        }
+      }
+      const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0) || (key0 + kBC > wi.seq_len);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool dead = key >= wi.seq_len || (CAUSAL && key > qi);
+            if (dead) s[kb][r] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = wave_max_halves(mx) * p.c;
+      const float m_new = fmaxf(m_ref, mx);
+      const bool grow = m_new > m_ref + kTau;
+      if (__ballot(grow) != 0ull) {
+        // rescale the whole wave to the new reference (lanes whose max did not
+        // move get alpha = 1); a row that has seen no key yet keeps -inf
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(s[kb][r], p.c, -m_use));
+          s[kb][r] = pv;
+          lsum += pv;
+        }
+      // O^T += V^T P^T over four 16-key chunks
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const bf16x8 pb = frag_rows(s[kc >> 1], kc & 1);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 a = as_bf16x8(ld_lds16(vt + (db * 32 + l32) * L::vStride + kc * 32 + half * 16));
+          oacc[db] = mfma32x32x16(a, pb, oacc[db]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (!q_ok) return;
+  const float inv = 1.0f / ltot;
+  bf16* orow = p.o + ((long)wi.seq_start + qi) * q_row + (long)wi.h * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * half;
+      u32x2 w;
+      w[0] = pack2_bf16(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+      w[1] = pack2_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + d0) = w;
+    }
+  if (half == 0) {
+    const float lse = (m_ref + log2f(ltot)) * kLn2;
+    long idx;
+    if (VARLEN) idx = (long)wi.h * p.T + wi.seq_start + qi;
+    else idx = ((long)wi.b * p.Hq + wi.h) * p.N + qi;
+    p.lse[idx] = lse;
+  }
+}
+
+template <int D, int NW, bool CAUSAL, bool VARLEN>
+hipError_t launch_fwd_t(const FwdParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VARLEN>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int fwd_tile_rows() { return kFwdWaves * 32; }
+int fwd_tile_keys() { return kBC; }
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,
+                      hipStream_t stream) {
+  constexpr int NW = kFwdWaves;
+  if (d == 128) {
+    if (causal) return varlen ? launch_fwd_t<128, NW, true, true>(p, grid, stream)
+                              : launch_fwd_t<128, NW, true, false>(p, grid, stream);
+    return varlen ? launch_fwd_t<128, NW, false, true>(p, grid, stream)
+                  : launch_fwd_t<128, NW, false, false>(p, grid, stream);
+  }
+  if (causal) return varlen ? launch_fwd_t<64, NW, true, true>(p, grid, stream)
+                            : launch_fwd_t<64, NW, true, false>(p, grid, stream);
+  return varlen ? launch_fwd_t<64, NW, false, true>(p, grid, stream)
+                : launch_fwd_t<64, NW, false, false>(p, grid, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,43 @@
+// fa_launch.h -- host-side launch entry points of the kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fa_common.h"
+
+namespace fa {
+
+constexpr int kFwdWaves = 8;   // forward workgroup: 8 waves, 256 query rows
+constexpr int kBwdWaves = 4;   // backward workgroup: 4 waves, 128 keys
+constexpr int kBwdBQ = 32;     // backward query tile
+constexpr int kBwdBC = kBwdWaves * 32;
+
+int fwd_tile_rows();
+int fwd_tile_keys();
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,
+                      hipStream_t stream);
+
+// D = rowsum(dO o O) in the logsumexp layout; zeroes the fp32 dQ accumulator,
+// the semaphores and the workspace header.
+hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, float* dvec, float* dq_acc,
+                          int* sem, long sem_count, uint32_t* hdr, int rows, int Hq, int d,
+                          bool varlen, int N, int T, hipStream_t stream);
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, bool det, int grid,
+                      hipStream_t stream);
+
+// dQ = bf16(scale * dQ_acc); when S > 1 also dK/dV = bf16(sum of the S partials).
+hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float scale,
+                           const float* dk_part, const float* dv_part, bf16* dk, bf16* dv,
+                           long kv_elems, int S, hipStream_t stream);
+
+// Variable-length scheduler: validates cu_seqlens and writes the ordered work list.
+//   mode 0: forward query tiles, longest first
+//   mode 1: backward key tiles, longest first
+//   mode 2: backward key tiles, deterministic order (key tiles of a sequence last-first)
+hipError_t launch_sched(const int* cu_seqlens, int nseq, int total, int tile, int mode,
+                        bool causal, int fwd_kv_tile, int bwd_q_tile, int* tiles, int max_tiles,
+                        uint32_t* hdr, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,221 @@
+"""Thin ctypes binding of libfa_mi355x.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module only checks
+tensor shapes and dtypes, allocates outputs and workspaces with PyTorch, and
+passes raw device pointers plus the current HIP stream.  Importing it fails
+loudly when the library has not been built: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m exact_attention_80_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "fa_abi_version": ([], _i),
+    "fa_status_string": ([_i], ctypes.c_char_p),
+    "fa_last_error": ([], ctypes.c_char_p),
+    "fa_fwd_workspace_size": ([_i] * 6, _sz),
+    "fa_fwd": ([_p] * 5 + [_i] * 5 + [_f, _i, _p, _sz, _p], _i),
+    "fa_bwd_workspace_size": ([_i] * 7, _sz),
+    "fa_bwd": ([_p] * 9 + [_i] * 5 + [_f, _i, _i, _p, _sz, _p], _i),
+    "fa_varlen_fwd_workspace_size": ([_i] * 6, _sz),
+    "fa_varlen_fwd": ([_p] * 6 + [_i] * 6 + [_f, _i, _p, _sz, _p], _i),
+    "fa_varlen_bwd_workspace_size": ([_i] * 7, _sz),
+    "fa_varlen_bwd": ([_p] * 10 + [_i] * 6 + [_f, _i, _i, _p, _sz, _p], _i),
+    "fa_workspace_error": ([_p, _sz, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
+}
+for _name, (_args, _ret) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+FA_OK = 0
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = _lib.fa_status_string(status).decode()
+        detail = _lib.fa_last_error().decode()
+        super().__init__(f"{where}: {name}: {detail}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, shape, dtype=torch.bfloat16):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _scale(d, softmax_scale):
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None):
+    """Dense forward: q [B,N,Hq,d], k/v [B,N,Hkv,d] bf16 -> (o [B,N,Hq,d] bf16, lse [B,Hq,N] fp32)."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _need(q, "q", (B, N, Hq, d))
+    _need(k, "k", (B, N, Hkv, d))
+    _need(v, "v", (B, N, Hkv, d))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    ws_n = _lib.fa_fwd_workspace_size(B, N, Hq, Hkv, d, int(causal))
+    ws = _workspace(ws_n, q.device)
+    _check(_lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
+                       _ptr(ws), ws_n, _stream()), "fa_fwd")
+    return o, lse
+
+
+def bwd_workspace(q, k, causal: bool, deterministic: bool) -> torch.Tensor:
+    B, N, Hq, d = q.shape
+    n = _lib.fa_bwd_workspace_size(B, N, Hq, k.shape[2], d, int(causal), int(deterministic))
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None = None,
+        deterministic: bool = False, workspace: torch.Tensor | None = None):
+    """Dense backward -> (dq [B,N,Hq,d], dk [B,N,Hkv,d], dv [B,N,Hkv,d]) bf16."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _need(q, "q", (B, N, Hq, d))
+    _need(k, "k", (B, N, Hkv, d))
+    _need(v, "v", (B, N, Hkv, d))
+    _need(o, "o", (B, N, Hq, d))
+    _need(do, "do", (B, N, Hq, d))
+    _need(lse, "lse", (B, Hq, N), torch.float32)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = bwd_workspace(q, k, causal, deterministic) if workspace is None else workspace
+    _check(_lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal), int(deterministic),
+                       ws.data_ptr(), ws.numel(), _stream()), "fa_bwd")
+    return dq, dk, dv
+
+
+def _cu(cu_seqlens, T):
+    _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32)
+    return cu_seqlens.shape[0] - 1
+
+
+def varlen_fwd_workspace(nseq: int, T: int, Hq: int, Hkv: int, d: int, causal: bool,
+                         device) -> torch.Tensor | None:
+    return _workspace(_lib.fa_varlen_fwd_workspace_size(nseq, T, Hq, Hkv, d, int(causal)), device)
+
+
+def varlen_bwd_workspace(nseq: int, T: int, Hq: int, Hkv: int, d: int, causal: bool,
+                         deterministic: bool, device) -> torch.Tensor:
+    n = _lib.fa_varlen_bwd_workspace_size(nseq, T, Hq, Hkv, d, int(causal), int(deterministic))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, softmax_scale: float | None = None,
+               max_seqlen: int = 0, workspace: torch.Tensor | None = None):
+    """Packed forward: q [T,Hq,d], k/v [T,Hkv,d], cu_seqlens int32 [nseq+1] on the device
+    -> (o [T,Hq,d], lse [Hq,T])."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", (T, Hq, d))
+    _need(k, "k", (T, Hkv, d))
+    _need(v, "v", (T, Hkv, d))
+    nseq = _cu(cu_seqlens, T)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    ws = workspace
+    if ws is None:
+        ws = varlen_fwd_workspace(nseq, T, Hq, Hkv, d, causal, q.device)
+    _check(_lib.fa_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), cu_seqlens.data_ptr(), nseq, T, int(max_seqlen),
+                              Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
+                              _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+           "fa_varlen_fwd")
+    return o, lse
+
+
+def varlen_bwd(q, k, v, o, lse, do, cu_seqlens, causal: bool = False,
+               softmax_scale: float | None = None, deterministic: bool = False,
+               max_seqlen: int = 0, workspace: torch.Tensor | None = None):
+    """Packed backward -> (dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d])."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", (T, Hq, d))
+    _need(k, "k", (T, Hkv, d))
+    _need(v, "v", (T, Hkv, d))
+    _need(o, "o", (T, Hq, d))
+    _need(do, "do", (T, Hq, d))
+    _need(lse, "lse", (Hq, T), torch.float32)
+    nseq = _cu(cu_seqlens, T)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = workspace
+    if ws is None:
+        ws = varlen_bwd_workspace(nseq, T, Hq, Hkv, d, causal, deterministic, q.device)
+    _check(_lib.fa_varlen_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), cu_seqlens.data_ptr(), nseq, T, int(max_seqlen),
+                              Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
+                              int(deterministic), ws.data_ptr(), ws.numel(), _stream()),
+           "fa_varlen_bwd")
+    return dq, dk, dv
+
+
+def workspace_error(ws: torch.Tensor) -> int:
+    """Synchronise and return the device error word a varlen/backward call left in ``ws``."""
+    bits = ctypes.c_uint32(0)
+    st = _lib.fa_workspace_error(ws.data_ptr(), ws.numel(), _stream(), ctypes.byref(bits))
+    if st not in (FA_OK, 6):
+        _check(st, "fa_workspace_error")
+    return int(bits.value)
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def raw():
+    """The ctypes handle of the library (for ABI tests)."""
+    return _lib

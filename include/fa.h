@@ -1,0 +1,166 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa_mi355x.so).
+ *
+ * The library computes exact scaled-dot-product attention, forward and backward,
+ * with hand-written HIP kernels; it never approximates the softmax.  The method
+ * follows the pages describing FlashAttention-2 and FlashAttention-4:
+ *   [FA2]  "FlashAttention-2: Faster Attention with Better Parallelism and Work
+ *          Partitioning (ICLR 2024)" (wiki summary), sections "Problem and
+ *          motivation" and "Core method" 1-4;
+ *   [FA4B] "FlashAttention-4 backward optimisation: 2-CTA mode and performance"
+ *          (blog), sections 2.1 (global atomics for dQ), 3.2 (semaphore-ordered
+ *          deterministic reduction), 3.3.1 (shortest-processing-time order for
+ *          the causal deterministic backward), 3.3.2 (longest-processing-time
+ *          order for variable-length batches), 5.2 (walk every query head of a
+ *          key/value head together), 5.3 (bf16 operands, fp32 accumulation);
+ *   [FA4N] "FlashAttention-4 wird offiziell veroeffentlicht" (news article),
+ *          section on the co-design ideas (conditional softmax rescaling).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are caller-owned DEVICE memory (e.g. PyTorch allocations), dense,
+ *    contiguous, 16-byte aligned.  Q, K, V, O, dO, dQ, dK, dV are bf16.
+ *    The library never allocates or frees device memory and keeps no state
+ *    beyond a per-device property cache, so calls on different streams are
+ *    independent as long as their buffers (including workspaces) differ.
+ *  - Dense layout (token-major): Q/O/dO/dQ are [B, N, Hq, d]; K/V/dK/dV are
+ *    [B, N, Hkv, d]; the logsumexp LSE is fp32 [B, Hq, N].
+ *  - Packed variable-length layout: Q/O/dO/dQ are [T, Hq, d], K/V/dK/dV are
+ *    [T, Hkv, d] and LSE is fp32 [Hq, T], where sequence s occupies tokens
+ *    cu_seqlens[s] .. cu_seqlens[s+1]-1.  cu_seqlens is DEVICE int32 with
+ *    nseq+1 entries; it is validated on the device (first 0, last T,
+ *    non-decreasing) and a violation is reported through the workspace error
+ *    word (fa_workspace_error), not by the return value.
+ *  - d (head dimension) is 64 or 128.  Hq must be a positive multiple of Hkv;
+ *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
+ *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2);
+ *    queries and keys always have the same length.
+ *  - softmax_scale multiplies q.k before the softmax (typically 1/sqrt(d)).
+ *  - LSE_i = ln sum_j exp(softmax_scale * q_i.k_j)  ([FA2] "Core method" 1:
+ *    the only statistic the backward needs).
+ *  - stream is a hipStream_t passed as void* (NULL = default stream).  Every
+ *    call is asynchronous on that stream; argument errors are detected on the
+ *    host and returned before anything is launched.
+ *  - ws / ws_bytes: caller-owned device workspace of at least the size that the
+ *    matching *_workspace_size query returns for the same arguments (ws may be
+ *    NULL when that size is 0).  Its contents on entry do not matter.
+ *  - Return value: an fa_status; fa_status_string() names it and
+ *    fa_last_error() gives the detailed message of the calling thread's last
+ *    failure.  No C++ exception ever crosses this interface.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,    /* null pointer, bad size, misalignment, bad flag */
+  FA_ERR_UNSUPPORTED = 2,    /* valid but not implemented (e.g. d not in {64,128}) */
+  FA_ERR_WORKSPACE = 3,      /* workspace missing or smaller than required */
+  FA_ERR_HIP = 4,            /* a HIP runtime call or kernel launch failed */
+  FA_ERR_DEVICE = 5,         /* current device is not a gfx950 GPU */
+  FA_ERR_DEVICE_REPORTED = 6 /* a kernel flagged an error in the workspace */
+} fa_status;
+
+/* Bits of the device-side error word read by fa_workspace_error(). */
+#define FA_DEVERR_BAD_CU_SEQLENS 1u  /* cu_seqlens not 0..T non-decreasing */
+#define FA_DEVERR_WAIT_TIMEOUT 2u    /* deterministic dQ ordering wait expired */
+#define FA_DEVERR_TILE_OVERFLOW 4u   /* more tiles than the workspace holds */
+
+/* Version of this interface (incremented on any incompatible change). */
+int fa_abi_version(void);
+
+/* Static name of a status code. */
+const char* fa_status_string(int status);
+
+/* Detailed message of the calling thread's most recent non-FA_OK return. */
+const char* fa_last_error(void);
+
+/* ---- dense forward ------------------------------------------------------ */
+
+/* Workspace bytes fa_fwd needs for these sizes (0: the dense forward needs none). */
+size_t fa_fwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal);
+
+/*
+ * Forward pass ([FA2] "Core method" 1-3, [FA4N] conditional rescaling):
+ *   O = softmax(scale * Q K^T [causal mask]) V,   LSE as defined above.
+ * q [B,N,Hq,d], k/v [B,N,Hkv,d] bf16 inputs; o [B,N,Hq,d] bf16 and
+ * lse [B,Hq,N] fp32 outputs.  The result does not depend on the launch order
+ * (every output element is written by exactly one workgroup).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int N, int Hq, int Hkv, int d, float softmax_scale, int causal,
+           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- dense backward ----------------------------------------------------- */
+
+/* Workspace bytes fa_bwd needs (fp32 dQ accumulator, D = rowsum(dO o O),
+ * ordering semaphores, split dK/dV partials). */
+size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
+                             int deterministic);
+
+/*
+ * Backward pass: from Q, K, V, the forward's O and LSE, and dO, computes
+ *   D = rowsum(dO o O), P = exp(scale Q K^T - LSE), dV = P^T dO,
+ *   dP = dO V^T, dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q,
+ * with dK/dV summed over the query heads of each key/value head
+ * ([FA2] "Core method" 2 and 4).  Work is split over key/value tiles; the
+ * partial dQ of every tile is reduced in fp32 with device atomics when
+ * deterministic == 0 ([FA4B] 2.1), or in a fixed order serialised by
+ * semaphores when deterministic == 1 ([FA4B] 3.2, 3.3.1), which makes
+ * dQ/dK/dV bit-identical from run to run.  dK/dV never use atomics.
+ * Outputs dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] bf16.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int N, int Hq, int Hkv, int d, float softmax_scale, int causal,
+           int deterministic, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- packed variable-length forward / backward ---------------------------- */
+
+/* max_seqlen: an upper bound on any sequence length, or 0 if unknown; it is only
+ * checked on the device.  total_tokens = T = cu_seqlens[nseq]. */
+size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
+                                    int causal);
+
+/*
+ * Forward over a packed batch: every sequence attends only to itself.  A
+ * one-workgroup scheduling kernel first reads cu_seqlens on the device and
+ * orders the (sequence, query-tile) work items longest-first ([FA4B] 3.3.2),
+ * so no host synchronisation is needed.  Shapes as in the packed layout above.
+ */
+int fa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
+                  int Hq, int Hkv, int d, float softmax_scale, int causal,
+                  void* ws, size_t ws_bytes, void* stream);
+
+size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
+                                    int causal, int deterministic);
+
+/* Backward over a packed batch; semantics as fa_bwd, per sequence. */
+int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
+                  int Hq, int Hkv, int d, float softmax_scale, int causal,
+                  int deterministic, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Debug/test helper: synchronises `stream`, reads the device error word that
+ * the last call using this workspace left, and returns FA_OK when it is clear
+ * or FA_ERR_DEVICE_REPORTED (fa_last_error() then names the FA_DEVERR_* bits).
+ * *bits (if not NULL) receives the raw word.  ws must be a workspace of a
+ * varlen call or a backward call.
+ */
+int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library loads without a GPU, exports every symbol include/fa.h
+declares, and rejects bad arguments on the host before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = 0x10000          # a 16-byte aligned non-null address (never dereferenced)
+MIS = 0x10008        # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_attention_80_amd import build
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    L = ctypes.CDLL(build.LIB_PATH)
+    p, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [p] * 5 + [i] * 5 + [f, i, p, sz, p]
+    L.fa_bwd.argtypes = [p] * 9 + [i] * 5 + [f, i, i, p, sz, p]
+    L.fa_varlen_fwd.argtypes = [p] * 6 + [i] * 6 + [f, i, p, sz, p]
+    L.fa_varlen_bwd.argtypes = [p] * 10 + [i] * 6 + [f, i, i, p, sz, p]
+    L.fa_bwd_workspace_size.argtypes = [i] * 7
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_fwd_workspace_size.argtypes = [i] * 6
+    L.fa_fwd_workspace_size.restype = sz
+    L.fa_varlen_fwd_workspace_size.argtypes = [i] * 6
+    L.fa_varlen_fwd_workspace_size.restype = sz
+    L.fa_varlen_bwd_workspace_size.argtypes = [i] * 7
+    L.fa_varlen_bwd_workspace_size.restype = sz
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_workspace_error.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_uint32)]
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_fwd_workspace_size",
+              "fa_bwd_workspace_size", "fa_status_string", "fa_workspace_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_names(lib):
+    assert lib.fa_abi_version() == 1
+    assert lib.fa_status_string(0) == b"FA_OK"
+    assert lib.fa_status_string(3) == b"FA_ERR_WORKSPACE"
+    assert lib.fa_status_string(99) == b"FA_ERR_UNKNOWN"
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, N=128, Hq=2, Hkv=2, d=64, scale=0.125, causal=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, N, Hq, Hkv, d, scale, causal, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(lse=None), INVALID),
+    (dict(o=MIS), INVALID), (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(N=-3), INVALID),
+    (dict(Hq=3, Hkv=2), INVALID), (dict(Hkv=0), INVALID), (dict(causal=2), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.fa_last_error()
+
+
+def bwd(lib, ws=P, ws_bytes=None, det=0, d=64, dq=P, B=1, N=128, Hq=2, Hkv=2):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 0, det)
+    return lib.fa_bwd(P, P, P, P, P, P, dq, P, P, B, N, Hq, Hkv, d, 0.125, 0, det, ws, ws_bytes, None)
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    assert bwd(lib, ws=None) == WORKSPACE
+    assert bwd(lib, ws_bytes=16) == WORKSPACE
+    assert bwd(lib, det=2) == INVALID
+    assert bwd(lib, dq=None) == INVALID
+    assert bwd(lib, d=80) == UNSUPPORTED
+    assert bwd(lib, ws=MIS) == INVALID
+
+
+def test_workspace_sizes(lib):
+    B, N, Hq, Hkv, d = 2, 1000, 8, 2, 128
+    assert lib.fa_fwd_workspace_size(B, N, Hq, Hkv, d, 1) == 0
+    fast = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 0)
+    det = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 1)
+    assert fast >= B * N * Hq * d * 4 + B * N * Hq * 4  # fp32 dQ accumulator + D
+    assert det > fast                                    # plus the semaphores
+    assert lib.fa_bwd_workspace_size(B, N, 3, 2, d, 1, 0) == 0
+    vf = lib.fa_varlen_fwd_workspace_size(5, 4000, Hq, Hkv, d, 1)
+    vb = lib.fa_varlen_bwd_workspace_size(5, 4000, Hq, Hkv, d, 1, 1)
+    assert vf >= 256 and vb >= 4000 * Hq * d * 4
+    assert lib.fa_varlen_fwd_workspace_size(0, 4000, Hq, Hkv, d, 1) == 0
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    ws_n = lib.fa_varlen_fwd_workspace_size(3, 300, 2, 2, 64, 1)
+    assert lib.fa_varlen_fwd(P, P, P, P, P, P, 0, 300, 0, 2, 2, 64, 0.1, 1, P, ws_n, None) == INVALID
+    assert lib.fa_varlen_fwd(P, P, P, P, P, None, 3, 300, 0, 2, 2, 64, 0.1, 1, P, ws_n, None) == INVALID
+    assert lib.fa_varlen_fwd(P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, P, 8, None) == WORKSPACE
+    assert lib.fa_varlen_fwd(P, P, P, P, P, P, 3, 300, -1, 2, 2, 64, 0.1, 1, P, ws_n, None) == INVALID
+    wb = lib.fa_varlen_bwd_workspace_size(3, 300, 2, 2, 64, 1, 1)
+    assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 1, P, wb - 1,
+                             None) == WORKSPACE
+    assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 0, 0, 2, 2, 64, 0.1, 1, 1, P, wb,
+                             None) == INVALID
+
+
+def test_workspace_error_rejects_null(lib):
+    assert lib.fa_workspace_error(None, 0, None, None) == INVALID
+
+
+def test_binding_has_no_fallback():
+    """The Python binding only marshals arguments; it loads the HIP library and
+    never imports the oracle."""
+    src = open(os.path.join(ROOT, "exact_attention_80_amd", "fa.py")).read()
+    assert "oracle" not in src
+    assert "numpy" not in src

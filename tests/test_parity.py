@@ -1,0 +1,172 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded bf16 inputs, element by element, at sizes that span several
+tiles and ragged tails, plus GQA/MQA, packed variable-length batches and the
+deterministic mode."""
+
+import numpy as np
+import pytest
+
+from exact_attention_80_amd import inputs
+from oracle import attention as ora
+
+from gpu_helpers import (TOL_GRAD, TOL_LSE, TOL_O, max_abs, rel_fro, say, scale_for, to_dev,
+                         to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available()
+    from exact_attention_80_amd import fa as _fa
+    return _fa
+
+
+def run_dense(fa, B, N, Hq, Hkv, d, causal, seed=0, deterministic=False):
+    say(f"dense B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal} det={deterministic} seed={seed}")
+    x = inputs.dense_inputs(B, N, Hq, Hkv, d, seed=seed)
+    t = {n: to_dev(x[n]) for n in ("q", "k", "v", "do")}
+    sc = scale_for(d)
+    o, lse = fa.fwd(t["q"], t["k"], t["v"], causal=causal, softmax_scale=sc)
+    dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=causal, softmax_scale=sc,
+                        deterministic=deterministic)
+    return x, t, (o, lse, dq, dk, dv)
+
+
+def check_against_oracle(x, outs, causal, d):
+    o, lse, dq, dk, dv = (to_host(a) for a in outs)
+    sc = scale_for(d)
+    ro, rlse = ora.attention_forward(x["q"], x["k"], x["v"], sc, causal)
+    rdq, rdk, rdv = ora.attention_backward(x["q"], x["k"], x["v"], x["do"], sc, causal)
+    errs = dict(o=max_abs(o, ro), lse=max_abs(lse, rlse), dq=rel_fro(dq, rdq),
+                dk=rel_fro(dk, rdk), dv=rel_fro(dv, rdv))
+    say(f"errors {errs}")
+    assert errs["o"] <= TOL_O
+    assert errs["lse"] <= TOL_LSE
+    assert errs["dq"] <= TOL_GRAD
+    assert errs["dk"] <= TOL_GRAD
+    assert errs["dv"] <= TOL_GRAD
+
+
+DENSE_CASES = [
+    # (B, N, Hq, Hkv, d): the tiny configuration, ragged tails, GQA, MQA, single token
+    (1, 128, 2, 2, 64),
+    (1, 200, 2, 2, 64),
+    (2, 333, 4, 4, 128),
+    (1, 1, 2, 1, 128),
+    (1, 17, 3, 1, 64),
+    (2, 300, 8, 2, 128),
+    (1, 260, 4, 1, 64),
+    (1, 1024, 4, 2, 128),
+    (1, 777, 2, 2, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", DENSE_CASES, ids=lambda s: "x".join(map(str, s)))
+def test_dense_parity(fa, shape, causal):
+    B, N, Hq, Hkv, d = shape
+    x, _, outs = run_dense(fa, B, N, Hq, Hkv, d, causal)
+    check_against_oracle(x, outs, causal, d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_parity_deterministic(fa, causal):
+    x, _, outs = run_dense(fa, 2, 451, 6, 2, 128, causal, seed=3, deterministic=True)
+    check_against_oracle(x, outs, causal, 128)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 513, 4, 2, 128), (1, 640, 2, 1, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_deterministic_is_bit_identical(fa, shape, causal):
+    import torch
+    B, N, Hq, Hkv, d = shape
+    x, t, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=5, deterministic=True)
+    o, lse = outs[0], outs[1]
+    ref = [a.clone() for a in outs[2:]]
+    for rep in range(10):
+        g = fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=causal,
+                   softmax_scale=scale_for(d), deterministic=True)
+        for a, b in zip(g, ref):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rep
+    o2, lse2 = fa.fwd(t["q"], t["k"], t["v"], causal=causal, softmax_scale=scale_for(d))
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(lse2, lse)
+
+
+def test_forward_independent_of_tile_order(fa, monkeypatch):
+    import torch
+    x = inputs.dense_inputs(2, 700, 8, 2, 128, seed=2)
+    t = {n: to_dev(x[n]) for n in ("q", "k", "v")}
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    monkeypatch.setenv("FA_SCHED", "natural")
+    o2, l2 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def run_varlen(fa, lengths, Hq, Hkv, d, causal, deterministic=False, seed=0):
+    import torch
+    say(f"varlen lengths={lengths} Hq={Hq} Hkv={Hkv} d={d} causal={causal} det={deterministic}")
+    x = inputs.varlen_inputs(lengths, Hq, Hkv, d, seed=seed)
+    t = {n: to_dev(x[n]) for n in ("q", "k", "v", "do")}
+    cu = torch.from_numpy(x["cu_seqlens"]).to("cuda")
+    sc = scale_for(d)
+    o, lse = fa.varlen_fwd(t["q"], t["k"], t["v"], cu, causal=causal, softmax_scale=sc)
+    dq, dk, dv = fa.varlen_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], cu, causal=causal,
+                               softmax_scale=sc, deterministic=deterministic)
+    return x, t, cu, (o, lse, dq, dk, dv)
+
+
+VARLEN_CASES = [
+    ([1, 5, 130, 257, 64, 600, 33], 4, 2, 128),
+    ([300, 1, 1000, 129], 2, 2, 64),
+    ([513], 3, 1, 128),
+]
+
+
+@pytest.mark.parametrize("det", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"n{len(c[0])}h{c[1]}{c[2]}d{c[3]}")
+def test_varlen_parity(fa, case, causal, det):
+    lengths, Hq, Hkv, d = case
+    x, _, _, outs = run_varlen(fa, lengths, Hq, Hkv, d, causal, det)
+    o, lse, dq, dk, dv = (to_host(a) for a in outs)
+    sc = scale_for(d)
+    cu = x["cu_seqlens"]
+    ro, rlse = ora.varlen_forward(x["q"], x["k"], x["v"], cu, sc, causal)
+    rdq, rdk, rdv = ora.varlen_backward(x["q"], x["k"], x["v"], x["do"], cu, sc, causal)
+    errs = dict(o=max_abs(o, ro), lse=max_abs(lse, rlse), dq=rel_fro(dq, rdq),
+                dk=rel_fro(dk, rdk), dv=rel_fro(dv, rdv))
+    say(f"errors {errs}")
+    assert errs["o"] <= TOL_O and errs["lse"] <= TOL_LSE
+    assert errs["dq"] <= TOL_GRAD and errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD
+
+
+def test_varlen_deterministic_bit_identical(fa):
+    import torch
+    lengths = [700, 3, 128, 1029, 64]
+    x, t, cu, outs = run_varlen(fa, lengths, 4, 1, 128, True, deterministic=True, seed=4)
+    o, lse = outs[0], outs[1]
+    ref = [a.clone() for a in outs[2:]]
+    for rep in range(10):
+        g = fa.varlen_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], cu, causal=True,
+                          softmax_scale=scale_for(128), deterministic=True)
+        for a, b in zip(g, ref):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rep
+
+
+def test_varlen_bad_cu_seqlens_is_reported(fa):
+    import torch
+    say("varlen bad cu_seqlens")
+    x = inputs.varlen_inputs([10, 20, 30], 2, 2, 64, seed=1)
+    t = {n: to_dev(x[n]) for n in ("q", "k", "v")}
+    bad = torch.tensor([0, 20, 10, 60], dtype=torch.int32, device="cuda")  # decreasing
+    ws = fa.varlen_fwd_workspace(3, 60, 2, 2, 64, True, "cuda")
+    fa.varlen_fwd(t["q"], t["k"], t["v"], bad, causal=True, workspace=ws)
+    assert fa.workspace_error(ws) & 1
+    good = torch.from_numpy(x["cu_seqlens"]).to("cuda")
+    fa.varlen_fwd(t["q"], t["k"], t["v"], good, causal=True, workspace=ws)
+    assert fa.workspace_error(ws) == 0
