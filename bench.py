@@ -1,0 +1,223 @@
+"""Benchmark: causal self-attention forward + backward on one MI355X.
+
+One step = one forward and one backward pass over one batch of the headline
+workload (B=2, H=16, N=8192, d=128, bf16, causal, fast-mode backward), with
+seeded synthetic inputs already resident in HBM.  Throughput counts the
+algorithmic FLOPs 4*B*H*N^2*d/2 (forward) + 2.5x that (backward).
+
+Prints one JSON line.  Besides the headline it carries:
+  roofline      the dominant kernel (the backward main kernel): algorithmic
+                FLOPs per launch / its average duration from HIP events recorded
+                on its own stream during the timed steps, against the dense bf16
+                MFMA peak; `traffic` is filled from rocprofv3 counters when given
+                with --traffic-file;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample (whole query
+                heads of the same workload) on this host's cores, scaled to the
+                metric's unit.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
+METRIC = "attention fwd+bwd TFLOPs/s (bf16, d=128, causal N=8K) and % of MFMA peak"
+
+
+def flops(B, N, H, d, causal):
+    f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+    return f, 2.5 * f
+
+
+def make_inputs(B, N, Hq, Hkv, d, seed=0):
+    import numpy as np
+    import torch
+
+    from exact_attention_80_amd import inputs
+    x = inputs.dense_inputs(B, N, Hq, Hkv, d, seed=seed)
+    out = {}
+    for n in ("q", "k", "v", "do"):
+        bits = inputs.bf16_bits(x[n]).view(np.int16)
+        out[n] = torch.from_numpy(np.ascontiguousarray(bits)).to("cuda").view(torch.bfloat16)
+    return out
+
+
+def cpu_baseline(B, N, Hq, Hkv, d, causal, budget_s):
+    """Oracle fwd+bwd on whole query heads until budget_s elapses (at least one head)."""
+    import numpy as np
+
+    from exact_attention_80_amd import inputs
+    from oracle import attention as ora
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    scale = 1.0 / math.sqrt(d)
+    g = np.random.Generator(np.random.PCG64(123))
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        qh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+        kh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+        vh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+        doh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+        ora.head_forward_backward(qh, kh, vh, doh, scale, causal)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or heads >= B * Hq:
+            break
+    f, b = flops(1, N, 1, d, causal)
+    tflops = heads * (f + b) / el / 1e12
+    return {
+        "value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{heads} of {B * Hq} query heads (N={N}, d={d}, causal) fwd+bwd in fp64, "
+                  f"{el:.1f} s; rate scaled by algorithmic FLOPs per head",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--B", type=int, default=2)
+    ap.add_argument("--N", type=int, default=8192)
+    ap.add_argument("--H", type=int, default=16)
+    ap.add_argument("--Hkv", type=int, default=0)
+    ap.add_argument("--d", type=int, default=128)
+    ap.add_argument("--non-causal", action="store_true")
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 disables it)")
+    ap.add_argument("--traffic-file", default="",
+                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the deterministic backward (reported as extras)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_attention_80_amd import fa
+
+    B, N, Hq, d = args.B, args.N, args.H, args.d
+    Hkv = args.Hkv or Hq
+    causal = not args.non_causal
+    det = args.deterministic
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.set_device(0)
+    x = make_inputs(B, N, Hq, Hkv, d)
+    ws = fa.bwd_workspace(x["q"], x["k"], causal, det)
+
+    def step():
+        o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
+        fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
+               deterministic=det, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    fa.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = fa.timing_end()
+
+    f_fwd, f_bwd = flops(B, N, Hq, d, causal)
+    ms_step = elapsed * 1e3 / args.steps
+    value = (f_fwd + f_bwd) / (elapsed / args.steps) / 1e12
+
+    n_fwd, ms_fwd = kt["fwd"]
+    n_bwd, ms_bwd = kt["bwd_main"]
+    n_pre, ms_pre = kt["bwd_pre"]
+    n_post, ms_post = kt["bwd_post"]
+    avg_bwd_ms = ms_bwd / max(1, n_bwd)
+    avg_fwd_ms = ms_fwd / max(1, n_fwd)
+    achieved = f_bwd / (avg_bwd_ms * 1e-3) / 1e12
+    traffic = None
+    if args.traffic_file and os.path.exists(args.traffic_file):
+        with open(args.traffic_file) as fh:
+            traffic = json.load(fh).get("bwd_main_bytes_per_launch")
+
+    extras = {
+        "fwd_kernel_ms": avg_fwd_ms,
+        "fwd_tflops": f_fwd / (avg_fwd_ms * 1e-3) / 1e12,
+        "fwd_pct_peak": 100.0 * f_fwd / (avg_fwd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "bwd_main_kernel_ms": avg_bwd_ms,
+        "bwd_pre_ms": ms_pre / max(1, n_pre),
+        "bwd_post_ms": ms_post / max(1, n_post),
+        "bwd_tflops": f_bwd / ((ms_bwd + ms_pre + ms_post) / max(1, n_bwd) * 1e-3) / 1e12,
+        "pct_of_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
+    }
+    if args.extra and not det:
+        wsd = fa.bwd_workspace(x["q"], x["k"], causal, True)
+        o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
+        for _ in range(3):
+            fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
+                   deterministic=True, workspace=wsd)
+        torch.cuda.synchronize()
+        fa.timing_begin()
+        for _ in range(args.steps):
+            fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
+                   deterministic=True, workspace=wsd)
+        kd = fa.timing_end()
+        det_ms = sum(kd[k][1] for k in ("bwd_pre", "bwd_main", "bwd_post")) / args.steps
+        fast_ms = (ms_bwd + ms_pre + ms_post) / max(1, n_bwd)
+        extras["det_bwd_tflops"] = f_bwd / (det_ms * 1e-3) / 1e12
+        extras["det_over_fast_speed"] = fast_ms / det_ms
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{'causal' if causal else 'non-causal'} self-attention forward+backward, "
+                        f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}, "
+                        f"{'deterministic' if det else 'atomic'} dQ reduction",
+            "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
+            "deterministic": det,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bwd_kernel (backward main)",
+            "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": traffic,
+        },
+        "extras": extras,
+    }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(B, N, Hq, Hkv, d, causal, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,6 +8,8 @@
 #include <mutex>
 #include <string>
 #include <unordered_map>
+#include <utility>
+#include <vector>
 
 #include "../../include/fa.h"
 #include "fa_launch.h"
@@ -88,6 +90,45 @@ int sched_mode() {
 uint32_t spin_limit() {
   const int v = env_int("FA_DET_SPIN_TICKS", 0);
   return v > 0 ? (uint32_t)v : 200000000u;  // 2 s
+}
+
+// ---------------------------------------------------------------------------
+// opt-in per-thread kernel timing (fa_timing_begin / fa_timing_end)
+
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> pool;  // reused across sessions
+  size_t used = 0;
+  std::vector<std::pair<int, size_t>> marks;  // (kind, index of the start event)
+};
+thread_local Timing g_timing;
+
+hipEvent_t timing_event() {
+  Timing& t = g_timing;
+  if (t.used == t.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    t.pool.push_back(e);
+  }
+  return t.pool[t.used++];
+}
+
+// Records a start event; returns a token for timing_stop (or -1 when off).
+long timing_start(int kind, hipStream_t s) {
+  Timing& t = g_timing;
+  if (!t.on) return -1;
+  const size_t idx = t.used;
+  hipEvent_t a = timing_event();
+  hipEvent_t b = timing_event();
+  if (!a || !b) return -1;
+  hipEventRecord(a, s);
+  t.marks.emplace_back(kind, idx);
+  return (long)idx;
+}
+
+void timing_stop(long token, hipStream_t s) {
+  if (token < 0) return;
+  hipEventRecord(g_timing.pool[(size_t)token + 1], s);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -237,8 +278,10 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
   if (varlen) {
     uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, lay.hdr));
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
+    const long tk = timing_start(4, s);
     e = fa::launch_sched(cu, nseq, (int)T, br, 0, causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ,
                          tiles, lay.max_tiles, hdr, s);
+    timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
     p.tiles = tiles;
@@ -250,7 +293,9 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
   }
   if (grid <= 0) return FA_OK;
   if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const long tk = timing_start(0, s);
   e = fa::launch_fwd(p, d, causal != 0, varlen, (int)grid, s);
+  timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return FA_OK;
 }
@@ -280,9 +325,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   float* dvec = reinterpret_cast<float*>(at(ws, lay.dvec));
   float* dq_acc = reinterpret_cast<float*>(at(ws, lay.dq_acc));
   int* sem = reinterpret_cast<int*>(at(ws, lay.sem));
+  long tk = timing_start(2, s);
   hipError_t e = fa::launch_bwd_pre(static_cast<const fa::bf16*>(o),
                                     static_cast<const fa::bf16*>(dout), dvec, dq_acc, sem,
                                     lay.sem_count, hdr, (int)(T * Hq), Hq, d, varlen, N, (int)T, s);
+  timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
 
   BwdParams p{};
@@ -314,8 +361,10 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   long grid;
   if (varlen) {
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
+    tk = timing_start(4, s);
     e = fa::launch_sched(cu, nseq, (int)T, fa::kBwdBC, deterministic ? 2 : 1, causal != 0,
                          fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles, hdr, s);
+    timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
     p.tiles = tiles;
@@ -327,12 +376,16 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   }
   if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   if (grid > 0) {
+    tk = timing_start(1, s);
     e = fa::launch_bwd(p, d, causal != 0, varlen, deterministic != 0, (int)grid, s);
+    timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
+  tk = timing_start(3, s);
   e = fa::launch_bwd_post(dq_acc, static_cast<fa::bf16*>(dq), T * Hq * d, scale, p.dk_part,
                           p.dv_part, static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
                           T * Hkv * d, lay.S, s);
+  timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward post launch");
   return FA_OK;
 }
@@ -422,6 +475,36 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (max_seqlen < 0) return fail(FA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
   return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, true, 1, 0, cu_seqlens, nseq, total_tokens,
                  Hq, Hkv, d, softmax_scale, causal, deterministic, ws, ws_bytes, stream);
+}
+
+int fa_timing_begin(void) {
+  Timing& t = g_timing;
+  t.on = true;
+  t.used = 0;
+  t.marks.clear();
+  return FA_OK;
+}
+
+int fa_timing_end(int* counts, float* ms) {
+  Timing& t = g_timing;
+  t.on = false;
+  if (counts)
+    for (int i = 0; i < FA_TIMING_KINDS; ++i) counts[i] = 0;
+  if (ms)
+    for (int i = 0; i < FA_TIMING_KINDS; ++i) ms[i] = 0.f;
+  for (const auto& m : t.marks) {
+    hipEvent_t a = t.pool[m.second], b = t.pool[m.second + 1];
+    hipError_t e = hipEventSynchronize(b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float x = 0.f;
+    e = hipEventElapsedTime(&x, a, b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    if (counts) counts[m.first] += 1;
+    if (ms) ms[m.first] += x;
+  }
+  t.marks.clear();
+  t.used = 0;
+  return FA_OK;
 }
 
 int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* bits) {

@@ -344,10 +344,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (VARLEN) sidx = (long)h * p.sem_slots + it.seq_start / BQ + it.seq + i;
       else sidx = ((long)it.seq * p.Hq + h) * p.nq + i;
       int* semp = p.sem + sidx;
+      // Wait for our turn.  The semaphore and the dQ accumulator are only ever
+      // touched by device-scope atomics, which are performed at the coherence
+      // point, so no cache invalidation or write-back is needed: the spin uses
+      // relaxed agent-scope loads and the adds below are issued after it.
       if (tid == 0) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         uint32_t polls = 0;
-        while (__hip_atomic_load(semp, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != rank) {
+        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != rank) {
           __builtin_amdgcn_s_sleep(2);
           if ((++polls & 63u) == 0) {
             const uint32_t err = __hip_atomic_load(&p.hdr[kHdrErr], __ATOMIC_RELAXED,
@@ -362,20 +366,19 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
       __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (wave < DQW) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int q = q0 + 8 * (x >> 2) + 4 * half + (x & 3);
-          if (q < it.seq_len) {
-            float* a = dq_base + (long)q * q_row;
-            *a = *a + acc[x];
-          }
+          if (q < it.seq_len)
+            __hip_atomic_fetch_add(dq_base + (long)q * q_row, acc[x], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      // every add of this workgroup has been performed before the release
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(semp, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_fetch_add(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();  // dS reads done; next tile staged
   }

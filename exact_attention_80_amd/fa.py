@@ -40,6 +40,8 @@ _SIGS = {
     "fa_varlen_bwd_workspace_size": ([_i] * 7, _sz),
     "fa_varlen_bwd": ([_p] * 10 + [_i] * 6 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_workspace_error": ([_p, _sz, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
+    "fa_timing_begin": ([], _i),
+    "fa_timing_end": ([ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)], _i),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -210,6 +212,23 @@ def workspace_error(ws: torch.Tensor) -> int:
     if st not in (FA_OK, 6):
         _check(st, "fa_workspace_error")
     return int(bits.value)
+
+
+TIMING_KINDS = ("fwd", "bwd_main", "bwd_pre", "bwd_post", "sched")
+
+
+def timing_begin() -> None:
+    """Start recording HIP events around every kernel this thread launches."""
+    _check(_lib.fa_timing_begin(), "fa_timing_begin")
+
+
+def timing_end() -> dict:
+    """Stop recording; returns {kind: (launches, total_ms)} for the kernels launched since."""
+    n = len(TIMING_KINDS)
+    counts = (ctypes.c_int * n)()
+    ms = (ctypes.c_float * n)()
+    _check(_lib.fa_timing_end(counts, ms), "fa_timing_end")
+    return {k: (int(counts[i]), float(ms[i])) for i, k in enumerate(TIMING_KINDS)}
 
 
 def lib_path() -> str:

@@ -159,6 +159,23 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
  */
 int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* bits);
 
+/* ---- measurement ----------------------------------------------------------
+ * Opt-in kernel timing for benchmarks (not needed for correctness).  Between
+ * fa_timing_begin() and fa_timing_end(), every forward / backward call made by
+ * the calling thread records a pair of HIP events on its own stream around
+ * each kernel it launches.  fa_timing_end() waits for the last event and
+ * returns, per kernel kind, the number of launches and their summed duration
+ * in milliseconds:
+ *   kind 0: forward kernel;  kind 1: backward main kernel;
+ *   kind 2: backward preprocess (D = rowsum(dO o O), zeroing);
+ *   kind 3: backward post (dQ conversion, split dK/dV sum);
+ *   kind 4: variable-length scheduler.
+ * counts / ms must each point to FA_TIMING_KINDS elements (or be NULL).
+ * Events are created lazily and reused; nothing is allocated on the device. */
+#define FA_TIMING_KINDS 5
+int fa_timing_begin(void);
+int fa_timing_end(int* counts, float* ms);
+
 #ifdef __cplusplus
 }
 #endif
