@@ -34,24 +34,6 @@ constexpr int NT = NW * 64;
 constexpr int BQ = kBwdBQ;
 constexpr int BC = kBwdBC;
 
-template <int D>
-struct BwdLds {
-  static constexpr int rowStride = D * 2 + 16;    // Q, dO row-major tiles
-  static constexpr int tStride = BQ * 2 + 16;     // Q^T, dO^T (permuted query axis)
-  static constexpr int sStride = BC * 2 + 16;     // dS [q][key]
-  static constexpr int ktStride = BC * 2 + 16;    // K^T [d][key]
-  static constexpr int qs = 0;
-  static constexpr int dos = qs + BQ * rowStride;
-  static constexpr int qt = dos + BQ * rowStride;
-  static constexpr int dot = qt + D * tStride;
-  static constexpr int lse = dot + D * tStride;
-  static constexpr int dvec = lse + BQ * 4;
-  static constexpr int ds = dvec + BQ * 4;
-  static constexpr int kt = ds + BQ * sStride;
-  static constexpr int misc = kt + D * ktStride;
-  static constexpr int total = misc + 16;
-};
-
 struct BwdItem {
   int seq;        // batch index (dense) or sequence index (varlen)
   int seq_start;
@@ -61,27 +43,53 @@ struct BwdItem {
   int jt;         // key tile
   int nq;         // query tiles of this sequence
   int nkv;        // key tiles of this sequence
-  bool valid;
+};
+
+// LDS plan.  K, Q and dO tiles are row-major with one padding chunk per row
+// and are filled by direct global->LDS loads (see PadTile); Q/dO/LSE/D are
+// double buffered.  dS^T is written by the waves with 8-byte stores into rows
+// of 80 bytes.  Total for d = 128: 34816 + 4 x 8704 + 512 + 10240 bytes, so
+// two workgroups fit in one CU's 160 KiB.
+template <int D>
+struct BwdLds {
+  static constexpr int CH = D / 8;
+  using KT = PadTile<BC, CH, CH + 1>;           // K tile [BC][D]
+  using QT = PadTile<BQ, CH, CH + 1>;           // Q or dO tile [BQ][D]
+  static constexpr int statBytes = 2 * BQ * 4;  // LSE[BQ] then D[BQ]
+  static constexpr int dsPitch = 80;            // dS^T row: 32 bf16 + padding
+  static constexpr int dsBytes = BC * dsPitch;
 };
 
 template <int D, bool CAUSAL, bool VARLEN, bool DET>
-__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kernel(BwdParams p) {
   using L = BwdLds<D>;
-  __shared__ __attribute__((aligned(16))) char smem[L::total];
-  int* sh_int = reinterpret_cast<int*>(smem + L::misc);
+  constexpr int CH = L::CH;
+  using KT = typename L::KT;
+  using QT = typename L::QT;
+  __shared__ __attribute__((aligned(16))) char k_s[KT::kBytes];
+  __shared__ __attribute__((aligned(16))) char q_s0[QT::kBytes];
+  __shared__ __attribute__((aligned(16))) char q_s1[QT::kBytes];
+  __shared__ __attribute__((aligned(16))) char do_s0[QT::kBytes];
+  __shared__ __attribute__((aligned(16))) char do_s1[QT::kBytes];
+  __shared__ __attribute__((aligned(16))) char st_s0[L::statBytes];
+  __shared__ __attribute__((aligned(16))) char st_s1[L::statBytes];
+  __shared__ __attribute__((aligned(16))) char ds_s[L::dsBytes];
+  __shared__ int sh_ticket;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  const int g16 = lane >> 4;
+  const int L16 = lane & 15;
 
   // ---------------- work item
   int r;
   if (DET) {
-    if (tid == 0) sh_int[0] = (int)atomicAdd(&p.hdr[kHdrTicket], 1u);
+    if (tid == 0) sh_ticket = (int)atomicAdd(&p.hdr[kHdrTicket], 1u);
     __syncthreads();
-    r = sh_int[0];
+    r = sh_ticket;
   } else {
     r = blockIdx.x;
   }
@@ -137,38 +145,18 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int wk0 = key0 + wave * 32;  // this wave's first key
   const int mykey = wk0 + l32;
   const bool key_ok = mykey < it.seq_len;
+  const int last = it.seq_len - 1;
 
-  // ---------------- K, V rows of this wave (operand B of S = Q K^T, dP = dO V^T)
+  // ---------------- K tile -> LDS (direct), V rows of this wave -> registers
   const bf16* kseq = p.k + (long)it.seq_start * kv_row + (long)it.hkv * D;
   const bf16* vseq = p.v + (long)it.seq_start * kv_row + (long)it.hkv * D;
-  bf16x8 kf[D / 16], vf[D / 16];
+  dma_tile<KT, CH, CH + 1, NW>(k_s, kseq, kv_row, key0, last, wave, lane);
+  bf16x8 vf[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key_ok) {
-      a = ld_global16(kseq + (long)mykey * kv_row + dc * 16 + half * 8);
-      b = ld_global16(vseq + (long)mykey * kv_row + dc * 16 + half * 8);
-    }
-    kf[dc] = as_bf16x8(a);
+    u32x4 b = {0u, 0u, 0u, 0u};
+    if (key_ok) b = ld_global16(vseq + (long)mykey * kv_row + dc * 16 + half * 8);
     vf[dc] = as_bf16x8(b);
-  }
-  // K^T of the whole key tile in LDS (operand B of dQ = dS K)
-  {
-    constexpr int KBL = (BC / 4) * (D / 8);
-#pragma unroll
-    for (int c = tid; c < KBL; c += NT) {
-      const int a = c % (BC / 4), bcol = c / (BC / 4);
-      u32x4 rows[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + 4 * a + e;
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (key < it.seq_len) u = ld_global16(kseq + (long)key * kv_row + bcol * 8);
-        rows[e] = u;
-      }
-      store_transposed_4x8(smem + L::kt + (bcol * 8) * L::ktStride, L::ktStride, (4 * a) * 2,
-                           rows[0], rows[1], rows[2], rows[3]);
-    }
   }
 
   f32x16 dk_acc[D / 32], dv_acc[D / 32];
@@ -182,89 +170,50 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int nsteps = max(0, it.nq - i_start);
   const int nitems = GS * nsteps;
 
-  // staging of one query tile: Q and dO rows (row-major and transposed), LSE, D
-  constexpr int QBL = (BQ / 4) * (D / 8);
-  static_assert(2 * QBL <= NT, "one staging block per thread");
-  u32x4 st[4];
-  float st_f = 0.f;
-  auto stage_load = [&](int item) {
+  // direct copy of one query tile's Q, dO rows and LSE, D values
+  auto issue_item = [&](int item, char* qd, char* dod, char* std_) {
     const int hh = item / nsteps;
     const int i = i_start + (item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
-    if (tid < 2 * QBL) {
-      const bool is_do = tid >= QBL;
-      const int c = is_do ? tid - QBL : tid;
-      const int a = c % (BQ / 4), bcol = c / (BQ / 4);
-      const bf16* src = (is_do ? p.dout : p.q) + (long)it.seq_start * q_row + (long)h * D;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int q = q0 + 4 * a + e;
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (q < it.seq_len) u = ld_global16(src + (long)q * q_row + bcol * 8);
-        st[e] = u;
-      }
-    }
-    if (tid < 2 * BQ) {
-      const int c = tid;
-      const bool is_d = c >= BQ;
-      const int q = q0 + (is_d ? c - BQ : c);
+    const bf16* qsrc = p.q + (long)it.seq_start * q_row + (long)h * D;
+    const bf16* dsrc = p.dout + (long)it.seq_start * q_row + (long)h * D;
+    dma_tile<QT, CH, CH + 1, NW>(qd, qsrc, q_row, q0, last, wave, lane);
+    dma_tile<QT, CH, CH + 1, NW>(dod, dsrc, q_row, q0, last, wave, lane);
+    if (wave == NW - 1) {
+      // lanes 0..31: LSE of the tile's rows, lanes 32..63: D
+      const int q = min(q0 + l32, last);
       long idx;
       if (VARLEN) idx = (long)h * p.T + it.seq_start + q;
       else idx = ((long)it.seq * p.Hq + h) * p.N + q;
-      if (q < it.seq_len) st_f = is_d ? p.dvec[idx] : p.lse[idx] * kLog2e;
-      else st_f = is_d ? 0.f : INFINITY;  // padding rows: P = 0, dS = 0
-    }
-  };
-  auto stage_store = [&]() {
-    if (tid < 2 * QBL) {
-      const bool is_do = tid >= QBL;
-      const int c = is_do ? tid - QBL : tid;
-      const int a = c % (BQ / 4), bcol = c / (BQ / 4);
-      char* rm = smem + (is_do ? L::dos : L::qs);
-      char* tr = smem + (is_do ? L::dot : L::qt);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st_lds16(rm + (4 * a + e) * L::rowStride + bcol * 16, st[e]);
-      store_transposed_4x8(tr + (bcol * 8) * L::tStride, L::tStride, kperm16(4 * a) * 2,
-                           st[0], st[1], st[2], st[3]);
-    }
-    if (tid < 2 * BQ) {
-      const int c = tid;
-      float* dst = reinterpret_cast<float*>(smem + (c >= BQ ? L::dvec : L::lse));
-      dst[c >= BQ ? c - BQ : c] = st_f;
+      dma4(half ? (const void*)(p.dvec + idx) : (const void*)(p.lse + idx), std_);
     }
   };
 
-  if (nitems > 0) {
-    stage_load(0);
-    stage_store();
-  }
-  __syncthreads();
-
-  for (int item = 0; item < nitems; ++item) {
+  auto compute_item = [&](int item, const char* qs, const char* dos, const char* sts) {
     const int hh = item / nsteps;
     const int i = i_start + (item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
-    if (item + 1 < nitems) stage_load(item + 1);
 
-    const bool active = key0 + wave * 32 < it.seq_len && (!CAUSAL || q0 + BQ - 1 >= wk0);
-    short* ds_tile = reinterpret_cast<short*>(smem + L::ds);
+    const bool active = wk0 < it.seq_len && (!CAUSAL || q0 + BQ - 1 >= wk0);
     if (active) {
       f32x16 s, dp;
 #pragma unroll
       for (int x = 0; x < 16; ++x) { s[x] = 0.f; dp[x] = 0.f; }
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        const bf16x8 aq = as_bf16x8(ld_lds16(smem + L::qs + l32 * L::rowStride + dc * 32 + half * 16));
-        const bf16x8 ado = as_bf16x8(ld_lds16(smem + L::dos + l32 * L::rowStride + dc * 32 + half * 16));
-        s = mfma32x32x16(aq, kf[dc], s);
+        const bf16x8 aq = as_bf16x8(ld_lds16(qs + QT::off(l32, 16 * dc + 8 * half)));
+        const bf16x8 bk = as_bf16x8(ld_lds16(k_s + KT::off(wave * 32 + l32, 16 * dc + 8 * half)));
+        const bf16x8 ado = as_bf16x8(ld_lds16(dos + QT::off(l32, 16 * dc + 8 * half)));
+        s = mfma32x32x16(aq, bk, s);
         dp = mfma32x32x16(ado, vf[dc], dp);
       }
       // s[x] = S[q = q0 + 8(x/4) + 4 half + x%4][key = mykey]
-      const float* lse_s = reinterpret_cast<const float*>(smem + L::lse);
-      const float* dv_s = reinterpret_cast<const float*>(smem + L::dvec);
-      const bool need_mask = (CAUSAL && q0 < wk0 + 31) || (wk0 + 32 > it.seq_len);
+      const float* lse_s = reinterpret_cast<const float*>(sts);
+      const float* dv_s = lse_s + BQ;
+      const bool need_mask = (CAUSAL && q0 < wk0 + 31) || (wk0 + 32 > it.seq_len) ||
+                             (q0 + BQ > it.seq_len);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * g + 4 * half);
@@ -272,55 +221,66 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int x = 4 * g + e;
-          float pr = fast_exp2(fmaf(s[x], p.c, -l4[e]));
+          float pr = fast_exp2(fmaf(s[x], p.c, -l4[e] * kLog2e));
           if (need_mask) {
             const int q = q0 + 8 * g + 4 * half + e;
-            if (!key_ok || (CAUSAL && mykey > q)) pr = 0.f;
+            if (!key_ok || q >= it.seq_len || (CAUSAL && mykey > q)) pr = 0.f;
           }
           s[x] = pr;
           dp[x] = pr * (dp[x] - d4[e]);
         }
       }
-      // dV += P^T dO and dK += dS^T Q over two 16-query chunks
+      // dV += P^T dO and dK += dS^T Q over two 16-query chunks; the B operands
+      // are transposed reads of the row-major dO / Q tiles, rows
+      // 16qc + 8ld + 4half + 0..3 matching the registers of P and dS
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
         const bf16x8 pa = frag_rows(s, qc);
         const bf16x8 dsa = frag_rows(dp, qc);
+        const int row0 = qc * 16 + 4 * (g16 >> 1) + (L16 >> 2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 bdo = as_bf16x8(ld_lds16(smem + L::dot + (db * 32 + l32) * L::tStride + qc * 32 + half * 16));
-          const bf16x8 bq = as_bf16x8(ld_lds16(smem + L::qt + (db * 32 + l32) * L::tStride + qc * 32 + half * 16));
+          const int col = db * 32 + 16 * (g16 & 1) + 4 * (L16 & 3);
+          const int o0 = QT::off(row0, col);
+          const int o1 = QT::off(row0 + 8, col);
+          const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
+          const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
           dv_acc[db] = mfma32x32x16(pa, bdo, dv_acc[db]);
           dk_acc[db] = mfma32x32x16(dsa, bq, dk_acc[db]);
         }
       }
-      // dS (bf16) to LDS as [q][key] for the workgroup-wide dQ product
+      // dS^T (bf16) rows of this wave's keys: 4 consecutive queries per store
+      char* dsrow = ds_s + (wave * 32 + l32) * L::dsPitch;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int q = 8 * (x >> 2) + 4 * half + (x & 3);
-        ds_tile[q * (L::sStride / 2) + wave * 32 + l32] =
-            (short)__builtin_bit_cast(unsigned short, (bf16)dp[x]);
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack2_bf16(dp[4 * g + 0], dp[4 * g + 1]);
+        w[1] = pack2_bf16(dp[4 * g + 2], dp[4 * g + 3]);
+        st_lds8(dsrow + (8 * g + 4 * half) * 2, w);
       }
     } else {
+      char* dsrow = ds_s + (wave * 32 + l32) * L::dsPitch;
+      const u32x2 z = {0u, 0u};
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int q = 8 * (x >> 2) + 4 * half + (x & 3);
-        ds_tile[q * (L::sStride / 2) + wave * 32 + l32] = 0;
-      }
+      for (int g = 0; g < 4; ++g) st_lds8(dsrow + (8 * g + 4 * half) * 2, z);
     }
-    __syncthreads();  // dS complete; Q/dO tiles no longer read
-    if (item + 1 < nitems) stage_store();
+    __syncthreads();  // dS^T complete
 
-    // ---------------- dQ_tile = dS K, reduced across key tiles
+    // ---------------- dQ_tile = dS K (this wave: columns 32w..32w+31)
     constexpr int DQW = D / 32;  // waves that own a 32-column block of dQ
     f32x16 acc;
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[x] = 0.f;
     if (wave < DQW) {
+      const int qcol = 16 * (g16 & 1) + 4 * (L16 & 3);
+      const int dcol = wave * 32 + qcol;
 #pragma unroll
       for (int kc = 0; kc < BC / 16; ++kc) {
-        const bf16x8 a = as_bf16x8(ld_lds16(smem + L::ds + l32 * L::sStride + kc * 32 + half * 16));
-        const bf16x8 b = as_bf16x8(ld_lds16(smem + L::kt + (wave * 32 + l32) * L::ktStride + kc * 32 + half * 16));
+        const int krow = kc * 16 + 8 * (g16 >> 1) + (L16 >> 2);
+        const bf16x8 a = cat8(ld_lds_tr8(ds_s + krow * L::dsPitch + qcol * 2),
+                              ld_lds_tr8(ds_s + (krow + 4) * L::dsPitch + qcol * 2));
+        const bf16x8 b = cat8(ld_lds_tr8(k_s + KT::off(krow, dcol)),
+                              ld_lds_tr8(k_s + KT::off(krow + 4, dcol)));
         acc = mfma32x32x16(a, b, acc);
       }
     }
@@ -376,11 +336,25 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
       // every add of this workgroup has been performed before the release
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmem();
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();  // dS reads done; next tile staged
+  };
+
+  // two-stage pipeline over the work items, unrolled so each LDS buffer is
+  // named statically: item t+1's rows are copied while item t is computed
+  if (nitems > 0) issue_item(0, q_s0, do_s0, st_s0);
+  for (int item = 0; item < nitems; item += 2) {
+    wait_vmem();
+    __syncthreads();  // item landed; every wave is past the previous item's reads
+    if (item + 1 < nitems) issue_item(item + 1, q_s1, do_s1, st_s1);
+    compute_item(item, q_s0, do_s0, st_s0);
+    if (item + 1 >= nitems) break;
+    wait_vmem();
+    __syncthreads();
+    if (item + 2 < nitems) issue_item(item + 2, q_s0, do_s0, st_s0);
+    compute_item(item + 1, q_s1, do_s1, st_s1);
   }
 
   // ---------------- dK = scale * sum dS^T Q, dV = sum P^T dO for this wave's keys

@@ -94,9 +94,91 @@ __device__ __forceinline__ u32x4 ld_lds16(const void* p) {
 __device__ __forceinline__ void st_lds16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st_lds8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
-__device__ __forceinline__ float wave_max_halves(float x) {
-  // lanes l and l^32 hold the two halves of the same query row
-  return fmaxf(x, __shfl_xor(x, 32));
+// Lanes l and l^32 hold the two halves of the same query row: combine them
+// with one v_permlane32_swap (each lane ends up with its own value in one
+// result and its partner's in the other).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles filled by direct global->LDS loads.
+//
+// A row-major tile of ROWS rows x CH 16-byte chunks is stored with a row pitch
+// of STRIDE >= CH chunks.  A direct load writes 64 consecutive 16-byte slots
+// per wave instruction, so slot s holds chunk s % STRIDE of row s / STRIDE; the
+// STRIDE - CH padding slots of a row are filled with a copy of its chunk 0 and
+// never read.  The padding staggers rows across the LDS banks while keeping
+// every operand address a per-lane base plus a compile-time offset.
+template <int ROWS, int CH, int STRIDE>
+struct PadTile {
+  static_assert(STRIDE >= CH, "row pitch");
+  static constexpr int kPitch = STRIDE * 16;           // bytes per row
+  static constexpr int kSlots = ROWS * STRIDE;
+  static constexpr int kBytes = kSlots * 16;
+  static constexpr int kInstr = (kSlots + 63) / 64;    // wave-wide loads per tile
+  __device__ static constexpr int off(int row, int col) { return row * kPitch + col * 2; }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// One wave-wide direct load: lane l copies 16 bytes from gsrc into
+// lds_wave_base + 16*l (lds_wave_base must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+// Same with 4 bytes per lane (lds_wave_base + 4*l).
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)gsrc, (lds_void_t*)lds_wave_base, 4, 0, 0);
+}
+
+// Direct copy of a padded tile (see PadTile): row r of the tile comes from
+// src + min(row0 + r, last) * src_row (rows past `last` repeat the last valid
+// row).  Wave w of NW issues the tile's wave-wide loads w, w + NW, ...
+template <class T, int CH, int STRIDE, int NW>
+__device__ __forceinline__ void dma_tile(char* dst, const __bf16* src, long src_row, int row0,
+                                         int last, int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < (T::kInstr + NW - 1) / NW; ++k) {
+    const int kk = k * NW + wave;
+    if (kk < T::kInstr) {
+      const int s = kk * 64 + lane;
+      if (s < T::kSlots) {
+        const int row = s / STRIDE;
+        int c = s - row * STRIDE;
+        if (c >= CH) c = 0;
+        dma16(src + (long)min(row0 + row, last) * src_row + c * 8, dst + kk * 1024);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i%4 of the 8-byte rows that lanes i/4,
+// i/4+4, i/4+8, i/4+12 of its group address.  If lane L of a group addresses
+// row base + L/4 at column nbase + 4*(L%4), lane i gets column nbase + i of
+// rows base .. base+3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ld_lds_tr8(const void* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ bf16x8 cat8(u32x2 a, u32x2 b) {
+  u32x4 u;
+  u[0] = a[0]; u[1] = a[1]; u[2] = b[0]; u[3] = b[1];
+  return as_bf16x8(u);
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

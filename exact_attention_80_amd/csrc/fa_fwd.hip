@@ -5,17 +5,20 @@
 //    the tiles are independent, so the output never depends on launch order;
 //  * split-Q: wave w owns query rows 32w..32w+31 of the tile and sees every
 //    key/value tile, so no reduction between waves is ever needed;
-//  * K/V tiles of 64 keys stream through LDS, double buffered: the global
-//    loads of tile j+1 are in flight while tile j is computed;
+//  * K and V tiles of 64 keys are copied global->LDS by direct loads (no
+//    register staging) into row-padded tiles, double buffered: tile j+1 is in
+//    flight while tile j is computed;
 //  * the score tile is computed transposed, S^T = K Q^T, so each lane holds one
-//    query column: the row max and row sum are in-lane plus one exchange with
-//    lane l^32;
+//    query column: the row max and row sum are in-lane plus one exchange
+//    between lane halves;
 //  * online softmax in base 2 with conditional rescaling: a stale reference max
 //    is kept and the accumulator is rescaled only when a row max grows by more
 //    than kTau (log2 units), decided per wave; probabilities therefore stay
 //    below 2^kTau and the result is unchanged;
-//  * the unscaled output accumulator O^T += V^T P^T stays in registers and is
-//    divided by the row sum once at the end; only LSE = ln(sum exp) is saved;
+//  * the unscaled output accumulator O^T += V^T P^T stays in registers (V^T is
+//    read from the row-major V tile with transposed LDS reads, in the key
+//    order the P fragment already has) and is divided by the row sum once at
+//    the end; only LSE = ln(sum exp) is saved;
 //  * causal: key tiles wholly above a wave's rows are skipped, the mask is
 //    applied only on tiles that straddle the diagonal or the sequence end.
 #include "fa_common.h"
@@ -28,15 +31,6 @@ namespace {
 constexpr int kBC = 64;        // keys per K/V tile
 constexpr float kTau = 8.0f;   // rescale threshold (log2 units): p <= 2^8
 
-template <int D>
-struct FwdTile {
-  static constexpr int kStride = D * 2 + 16;   // bytes per key row of the K tile
-  static constexpr int vStride = kBC * 2 + 16; // bytes per d row of the V^T tile
-  static constexpr int kBytes = kBC * kStride;
-  static constexpr int vBytes = D * vStride;
-  static constexpr int bufBytes = kBytes + vBytes;
-};
-
 struct WorkItem {
   int seq_start;  // first token of the sequence
   int seq_len;
@@ -46,7 +40,7 @@ struct WorkItem {
   bool valid;
 };
 
-template <bool CAUSAL, bool VARLEN, int BR>
+template <bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
   WorkItem w;
   const int t = blockIdx.x;
@@ -91,24 +85,26 @@ __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
 
 template <int D, int NW, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
-  constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
-  using L = FwdTile<D>;
-  constexpr int KCH = kBC * D / 8;     // 16-byte chunks in a K tile
-  constexpr int KIT = (KCH + NT - 1) / NT;
-  constexpr int VBL = (kBC / 4) * (D / 8);  // 4-key x 8-d blocks in a V tile
-  constexpr int VIT = (VBL + NT - 1) / NT;
+  constexpr int CH = D / 8;                      // 16-byte chunks per key row
+  using KT = PadTile<kBC, CH, CH + 1>;           // K: 16-byte operand reads
+  using VT = PadTile<kBC, CH, CH + 2>;           // V: 8-byte transposed reads
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::bufBytes];
+  __shared__ __attribute__((aligned(16))) char k0[KT::kBytes];
+  __shared__ __attribute__((aligned(16))) char k1[KT::kBytes];
+  __shared__ __attribute__((aligned(16))) char v0[VT::kBytes];
+  __shared__ __attribute__((aligned(16))) char v1[VT::kBytes];
 
-  const WorkItem wi = fwd_work_item<CAUSAL, VARLEN, BR>(p);
+  const WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
   if (!wi.valid) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  const int g16 = lane >> 4;   // 16-lane group
+  const int L16 = lane & 15;
 
   const int q0 = wi.qtile * BR;
   if (q0 >= wi.seq_len) return;
@@ -134,54 +130,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int kv_end = CAUSAL ? min(wi.seq_len, q0 + BR) : wi.seq_len;
   const int nt = (kv_end + kBC - 1) / kBC;
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kst[KIT];
-  u32x4 vst[VIT][4];
-  auto load_tile = [&](int j) {
-    const int key0 = j * kBC;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int c = tid + it * NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (c < KCH && key0 + row < wi.seq_len)
-        u = ld_global16(kbase + (long)(key0 + row) * kv_row + col * 8);
-      kst[it] = u;
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int c = tid + it * NT;
-      const int a = c & 15, bcol = c >> 4;  // keys 4a..4a+3, d 8*bcol..+7
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (c < VBL && key0 + 4 * a + r < wi.seq_len)
-          u = ld_global16(vbase + (long)(key0 + 4 * a + r) * kv_row + bcol * 8);
-        vst[it][r] = u;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kt = smem + buf * L::bufBytes;
-    char* vt = kt + L::kBytes;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int c = tid + it * NT;
-      if (c < KCH) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        st_lds16(kt + row * L::kStride + col * 16, kst[it]);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int c = tid + it * NT;
-      if (c < VBL) {
-        const int a = c & 15, bcol = c >> 4;
-        const int pos = kperm16(4 * a);  // 4 consecutive keys land contiguously
-        store_transposed_4x8(vt + (bcol * 8) * L::vStride, L::vStride, pos * 2,
-                             vst[it][0], vst[it][1], vst[it][2], vst[it][3]);
-      }
-    }
+  // ---- direct global->LDS copy of one K and one V tile (rows past the
+  // sequence end repeat the last valid row; their scores are masked)
+  auto issue_tile = [&](int j, char* kt, char* vt) {
+    dma_tile<KT, CH, CH + 1, NW>(kt, kbase, kv_row, j * kBC, wi.seq_len - 1, wave, lane);
+    dma_tile<VT, CH, CH + 2, NW>(vt, vbase, kv_row, j * kBC, wi.seq_len - 1, wave, lane);
   };
 
   // ---- running softmax state (per lane = per query; both lane halves agree)
@@ -193,86 +146,95 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   float m_ref = -INFINITY;  // reference max in scaled log2 units
   float lsum = 0.f;         // this lane half's partial row sum
 
-  if (nt > 0) load_tile(0);
-  for (int j = 0; j < nt; ++j) {
-    const int buf = j & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (j + 1 < nt) load_tile(j + 1);
-
+  auto compute_tile = [&](int j, const char* kt, const char* vt) {
     const int key0 = j * kBC;
     const bool active = !CAUSAL || key0 <= wq0 + 31;
-    if (active) {
-      const char* kt = smem + buf * L::bufBytes;
-      const char* vt = kt + L::kBytes;
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
+    if (!active) return;
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
+    for (int dc = 0; dc < D / 16; ++dc) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = as_bf16x8(ld_lds16(kt + (kb * 32 + l32) * L::kStride + dc * 32 + half * 16));
-          s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = as_bf16x8(ld_lds16(kt + KT::off(kb * 32 + l32, 16 * dc + 8 * half)));
+        s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
       }
-      const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0) || (key0 + kBC > wi.seq_len);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool dead = key >= wi.seq_len || (CAUSAL && key > qi);
-            if (dead) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = wave_max_halves(mx) * p.c;
-      const float m_new = fmaxf(m_ref, mx);
-      const bool grow = m_new > m_ref + kTau;
-      if (__ballot(grow) != 0ull) {
-        // rescale the whole wave to the new reference (lanes whose max did not
-        // move get alpha = 1); a row that has seen no key yet keeps -inf
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    }
+    const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0) || (key0 + kBC > wi.seq_len);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], p.c, -m_use));
-          s[kb][r] = pv;
-          lsum += pv;
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool dead = key >= wi.seq_len || (CAUSAL && key > qi);
+          if (dead) s[kb][r] = -INFINITY;
         }
-      // O^T += V^T P^T over four 16-key chunks
+    }
+    float mx = s[0][0];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 pb = frag_rows(s[kc >> 1], kc & 1);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a = as_bf16x8(ld_lds16(vt + (db * 32 + l32) * L::vStride + kc * 32 + half * 16));
-          oacc[db] = mfma32x32x16(a, pb, oacc[db]);
-        }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = halves_max(mx) * p.c;
+    const float m_new = fmaxf(m_ref, mx);
+    const bool grow = m_new > m_ref + kTau;
+    if (__ballot(grow) != 0ull) {
+      // rescale the whole wave to the new reference (lanes whose max did not
+      // move get alpha = 1); a row that has seen no key yet keeps -inf
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(fmaf(s[kb][r], p.c, -m_use));
+        s[kb][r] = pv;
+        lsum += pv;
+      }
+    // O^T += V^T P^T over four 16-key chunks; the transposed read of rows
+    // 16kc + 8ld + 4half + 0..3 gives exactly the keys of P's registers
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 pb = frag_rows(s[kc >> 1], kc & 1);
+      const int row0 = kc * 16 + 4 * (g16 >> 1) + (L16 >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int col = db * 32 + 16 * (g16 & 1) + 4 * (L16 & 3);
+        const u32x2 lo = ld_lds_tr8(vt + VT::off(row0, col));
+        const u32x2 hi = ld_lds_tr8(vt + VT::off(row0 + 8, col));
+        oacc[db] = mfma32x32x16(cat8(lo, hi), pb, oacc[db]);
       }
     }
+  };
+
+  // two-stage pipeline, unrolled so each LDS buffer is named statically
+  if (nt > 0) issue_tile(0, k0, v0);
+  for (int j = 0; j < nt; j += 2) {
+    wait_vmem();
+    __syncthreads();  // tile j landed for every wave; tile j-1's buffers are free
+    if (j + 1 < nt) issue_tile(j + 1, k1, v1);
+    compute_tile(j, k0, v0);
+    if (j + 1 >= nt) break;
+    wait_vmem();
+    __syncthreads();
+    if (j + 2 < nt) issue_tile(j + 2, k0, v0);
+    compute_tile(j + 1, k1, v1);
   }
 
   // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = halves_sum(lsum);
   if (!q_ok) return;
   const float inv = 1.0f / ltot;
   bf16* orow = p.o + ((long)wi.seq_start + qi) * q_row + (long)wi.h * D;
