@@ -104,6 +104,8 @@ def main():
                     help="JSON with measured HBM bytes per launch of the dominant kernel")
     ap.add_argument("--extra", action="store_true",
                     help="also time the deterministic backward (reported as extras)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -112,6 +114,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy_mib > 0:
+        # a plain copy of known size: reads and writes calibrate FETCH_SIZE / WRITE_SIZE
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n}), flush=True)
+        return
 
     from exact_attention_80_amd import fa
 

@@ -121,14 +121,14 @@ long timing_start(int kind, hipStream_t s) {
   hipEvent_t a = timing_event();
   hipEvent_t b = timing_event();
   if (!a || !b) return -1;
-  hipEventRecord(a, s);
+  (void)hipEventRecord(a, s);
   t.marks.emplace_back(kind, idx);
   return (long)idx;
 }
 
 void timing_stop(long token, hipStream_t s) {
   if (token < 0) return;
-  hipEventRecord(g_timing.pool[(size_t)token + 1], s);
+  (void)hipEventRecord(g_timing.pool[(size_t)token + 1], s);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

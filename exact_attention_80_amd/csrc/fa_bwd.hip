@@ -3,8 +3,8 @@
 // Method ([FA2] "Core method" 2 and 4; [FA4B] 2.1, 3.2, 3.3.1, 5.2, 5.3):
 //  * preprocess: D = rowsum(dO o O) per query row (fp32), and the fp32 dQ
 //    accumulator, the ordering semaphores and the workspace header are zeroed;
-//  * main kernel: one workgroup per (sequence, key/value head, key tile of 128
-//    keys, query-head subgroup).  Each of the 4 waves owns 32 keys and keeps its
+//  * main kernel: one workgroup per (sequence, key/value head, key tile of 256
+//    keys, query-head subgroup).  Each of the 8 waves owns 32 keys and keeps its
 //    K and V rows and its dK, dV accumulators in registers for the whole
 //    kernel.  The workgroup walks every query head of its key/value head
 //    (subgroup) and, per head, the 32-row query tiles from the diagonal
@@ -45,25 +45,35 @@ struct BwdItem {
   int nkv;        // key tiles of this sequence
 };
 
-// LDS plan.  K, Q and dO tiles are row-major with one padding chunk per row
-// and are filled by direct global->LDS loads (see PadTile); Q/dO/LSE/D are
-// double buffered.  dS^T is written by the waves with 8-byte stores into rows
-// of 80 bytes.  Total for d = 128: 34816 + 4 x 8704 + 512 + 10240 bytes, so
-// two workgroups fit in one CU's 160 KiB.
+// LDS plan.  K, Q and dO tiles are row-major SwzTiles (pitch 16 mod 64
+// dwords) filled by direct global->LDS loads; Q/dO/LSE/D are double
+// buffered.  dS^T is written by the waves with 8-byte stores into 64-byte rows
+// whose 8-byte slots are permuted by the row's quad index (conflict-free for
+// both the stores and the transposed reads).  The waves that own the second
+// key half of a dQ column block leave their partial sums in `part` for the
+// first half's wave to add before its atomics.  d = 128: 81920 + 4 x 10240 +
+// 512 + 16384 + 16384 bytes.
 template <int D>
 struct BwdLds {
   static constexpr int CH = D / 8;
-  using KT = PadTile<BC, CH, CH + 1>;           // K tile [BC][D]
-  using QT = PadTile<BQ, CH, CH + 1>;           // Q or dO tile [BQ][D]
-  static constexpr int statBytes = 2 * BQ * 4;  // LSE[BQ] then D[BQ]
-  static constexpr int dsPitch = 80;            // dS^T row: 32 bf16 + padding
+  static constexpr int STRIDE = D == 128 ? 20 : 12;  // pitch 320 or 192 bytes
+  using KT = SwzTile<BC, CH, STRIDE>;                // K tile [BC][D]
+  using QT = SwzTile<BQ, CH, STRIDE>;                // Q or dO tile [BQ][D]
+  static constexpr int statBytes = 2 * BQ * 4;       // LSE[BQ] then D[BQ]
+  static constexpr int dsPitch = BQ * 2;             // dS^T row: 32 bf16
   static constexpr int dsBytes = BC * dsPitch;
+  static constexpr int partBytes = (NW / 2) * 64 * 16 * 4;
 };
 
+// byte offset of the 8-byte slot holding dS^T[key][4s .. 4s+3]
+__device__ __forceinline__ int ds_off(int key, int s) {
+  return key * (BQ * 2) + ((s ^ ((key >> 2) & 7)) << 3);
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool DET>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   using L = BwdLds<D>;
-  constexpr int CH = L::CH;
+  constexpr int ST = L::STRIDE;
   using KT = typename L::KT;
   using QT = typename L::QT;
   __shared__ __attribute__((aligned(16))) char k_s[KT::kBytes];
@@ -74,6 +84,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __shared__ __attribute__((aligned(16))) char st_s0[L::statBytes];
   __shared__ __attribute__((aligned(16))) char st_s1[L::statBytes];
   __shared__ __attribute__((aligned(16))) char ds_s[L::dsBytes];
+  __shared__ __attribute__((aligned(16))) float part_s[L::partBytes / 4];
   __shared__ int sh_ticket;
 
   const int tid = threadIdx.x;
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // ---------------- K tile -> LDS (direct), V rows of this wave -> registers
   const bf16* kseq = p.k + (long)it.seq_start * kv_row + (long)it.hkv * D;
   const bf16* vseq = p.v + (long)it.seq_start * kv_row + (long)it.hkv * D;
-  dma_tile<KT, CH, CH + 1, NW>(k_s, kseq, kv_row, key0, last, wave, lane);
+  dma_swz_tile<KT, ST, NW>(k_s, kseq, kv_row, key0, last, wave, lane);
   bf16x8 vf[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
@@ -158,6 +169,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (key_ok) b = ld_global16(vseq + (long)mykey * kv_row + dc * 16 + half * 8);
     vf[dc] = as_bf16x8(b);
   }
+  wait_vmem();  // V rows and the K tile are in before the loop starts
 
   f32x16 dk_acc[D / 32], dv_acc[D / 32];
 #pragma unroll
@@ -178,17 +190,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int q0 = i * BQ;
     const bf16* qsrc = p.q + (long)it.seq_start * q_row + (long)h * D;
     const bf16* dsrc = p.dout + (long)it.seq_start * q_row + (long)h * D;
-    dma_tile<QT, CH, CH + 1, NW>(qd, qsrc, q_row, q0, last, wave, lane);
-    dma_tile<QT, CH, CH + 1, NW>(dod, dsrc, q_row, q0, last, wave, lane);
+    dma_swz_tile<QT, ST, NW>(qd, qsrc, q_row, q0, last, wave, lane);
+    dma_swz_tile<QT, ST, NW>(dod, dsrc, q_row, q0, last, wave, lane);
     if (wave == NW - 1) {
-      // lanes 0..31: LSE of the tile's rows, lanes 32..63: D
+      // lanes 0..31 copy the tile's LSE values, lanes 32..63 its D values;
+      // both land at std_ + 4*lane, so the buffer holds LSE[BQ] then D[BQ]
+      long base;
+      if (VARLEN) base = (long)h * p.T + it.seq_start;
+      else base = ((long)it.seq * p.Hq + h) * p.N;
       const int q = min(q0 + l32, last);
-      long idx;
-      if (VARLEN) idx = (long)h * p.T + it.seq_start + q;
-      else idx = ((long)it.seq * p.Hq + h) * p.N + q;
-      dma4(half ? (const void*)(p.dvec + idx) : (const void*)(p.lse + idx), std_);
+      if (half == 0) dma4(p.lse + base + q, std_);
+      else dma4(p.dvec + base + q, std_);
     }
   };
+
+  // dQ work split: wave w owns dQ column block (w & 3) over key half (w >> 2)
+  constexpr int DQB = D / 32;                // 32-column blocks of dQ
+  const int dq_blk = wave & 3;
+  const int dq_kh = wave >> 2;
+  const bool dq_wave = dq_blk < DQB;
+  const bool dq_issuer = dq_wave && dq_kh == 0;  // issues the atomics
+
+  // Per-lane LDS byte offsets.  Every operand read below is one of these
+  // bases plus a compile-time constant (the tile swizzle only permutes chunks
+  // inside aligned groups of four, so it never mixes with the unrolled loop
+  // indices).
+  //   16-byte reads of chunk 2dc + half of row r:  base[dc & 1] + 64 (dc >> 1)
+  const int q_rd[2] = {QT::off(l32, 8 * half), QT::off(l32, 16 + 8 * half)};
+  const int k_rd[2] = {KT::off(wave * 32 + l32, 8 * half), KT::off(wave * 32 + l32, 16 + 8 * half)};
+  //   transposed reads of Q/dO rows 16qc + 8ld + 4(g16/2) + L16/4, columns
+  //   32db + 16(g16%2) + 4(L16%4):  base[ld] + 16 qc pitch + 64 db
+  const int rq = 4 * (g16 >> 1) + (L16 >> 2);
+  const int cq = 16 * (g16 & 1) + 4 * (L16 & 3);
+  const int q_tr[2] = {QT::off(rq, cq), QT::off(rq + 8, cq)};
+  //   dQ phase, keys 128 kh + 16kc + 8(g16/2) + 4ld + L16/4:
+  //   K columns 32 blk + cq:  base[ld] + 16 kc pitch
+  //   dS^T slots of queries cq:  base[kc & 1][ld] + 2048 (kc >> 1)
+  const int rk = dq_kh * (BC / 2) + 8 * (g16 >> 1) + (L16 >> 2);
+  const int k_tr[2] = {KT::off(rk, dq_blk * 32 + cq), KT::off(rk + 4, dq_blk * 32 + cq)};
+  const int qslot = 4 * (g16 & 1) + (L16 & 3);
+  const int ds_tr[2][2] = {{ds_off(rk, qslot), ds_off(rk + 4, qslot)},
+                           {ds_off(rk + 16, qslot), ds_off(rk + 20, qslot)}};
 
   auto compute_item = [&](int item, const char* qs, const char* dos, const char* sts) {
     const int hh = item / nsteps;
@@ -203,12 +245,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int x = 0; x < 16; ++x) { s[x] = 0.f; dp[x] = 0.f; }
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        const bf16x8 aq = as_bf16x8(ld_lds16(qs + QT::off(l32, 16 * dc + 8 * half)));
-        const bf16x8 bk = as_bf16x8(ld_lds16(k_s + KT::off(wave * 32 + l32, 16 * dc + 8 * half)));
-        const bf16x8 ado = as_bf16x8(ld_lds16(dos + QT::off(l32, 16 * dc + 8 * half)));
+        const int qo = q_rd[dc & 1] + 64 * (dc >> 1);
+        const bf16x8 aq = as_bf16x8(ld_lds16(qs + qo));
+        const bf16x8 bk = as_bf16x8(ld_lds16(k_s + k_rd[dc & 1] + 64 * (dc >> 1)));
+        const bf16x8 ado = as_bf16x8(ld_lds16(dos + qo));
         s = mfma32x32x16(aq, bk, s);
         dp = mfma32x32x16(ado, vf[dc], dp);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounds register pressure
       // s[x] = S[q = q0 + 8(x/4) + 4 half + x%4][key = mykey]
       const float* lse_s = reinterpret_cast<const float*>(sts);
       const float* dv_s = lse_s + BQ;
@@ -237,63 +281,72 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int qc = 0; qc < 2; ++qc) {
         const bf16x8 pa = frag_rows(s, qc);
         const bf16x8 dsa = frag_rows(dp, qc);
-        const int row0 = qc * 16 + 4 * (g16 >> 1) + (L16 >> 2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int col = db * 32 + 16 * (g16 & 1) + 4 * (L16 & 3);
-          const int o0 = QT::off(row0, col);
-          const int o1 = QT::off(row0 + 8, col);
+          const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 64 * db;
+          const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 64 * db;
           const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
           const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
           dv_acc[db] = mfma32x32x16(pa, bdo, dv_acc[db]);
           dk_acc[db] = mfma32x32x16(dsa, bq, dk_acc[db]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       // dS^T (bf16) rows of this wave's keys: 4 consecutive queries per store
-      char* dsrow = ds_s + (wave * 32 + l32) * L::dsPitch;
+      const int krow = wave * 32 + l32;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
         w[0] = pack2_bf16(dp[4 * g + 0], dp[4 * g + 1]);
         w[1] = pack2_bf16(dp[4 * g + 2], dp[4 * g + 3]);
-        st_lds8(dsrow + (8 * g + 4 * half) * 2, w);
+        st_lds8(ds_s + ds_off(krow, 2 * g + half), w);
       }
     } else {
-      char* dsrow = ds_s + (wave * 32 + l32) * L::dsPitch;
+      const int krow = wave * 32 + l32;
       const u32x2 z = {0u, 0u};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) st_lds8(dsrow + (8 * g + 4 * half) * 2, z);
+      for (int g = 0; g < 4; ++g) st_lds8(ds_s + ds_off(krow, 2 * g + half), z);
     }
-    __syncthreads();  // dS^T complete
+    lds_barrier();  // dS^T complete (dQ atomics of the previous item may still be in flight)
 
-    // ---------------- dQ_tile = dS K (this wave: columns 32w..32w+31)
-    constexpr int DQW = D / 32;  // waves that own a 32-column block of dQ
+    // ---------------- dQ_tile = dS K: block (dq_blk) over keys 128 dq_kh .. +127
     f32x16 acc;
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[x] = 0.f;
-    if (wave < DQW) {
-      const int qcol = 16 * (g16 & 1) + 4 * (L16 & 3);
-      const int dcol = wave * 32 + qcol;
+    if (dq_wave) {
 #pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc) {
-        const int krow = kc * 16 + 8 * (g16 >> 1) + (L16 >> 2);
-        const bf16x8 a = cat8(ld_lds_tr8(ds_s + krow * L::dsPitch + qcol * 2),
-                              ld_lds_tr8(ds_s + (krow + 4) * L::dsPitch + qcol * 2));
-        const bf16x8 b = cat8(ld_lds_tr8(k_s + KT::off(krow, dcol)),
-                              ld_lds_tr8(k_s + KT::off(krow + 4, dcol)));
+      for (int kc = 0; kc < BC / 32; ++kc) {
+        const int dso = 2048 * (kc >> 1);
+        const int ko = 16 * kc * KT::kPitch;
+        const bf16x8 a = cat8(ld_lds_tr8(ds_s + ds_tr[kc & 1][0] + dso),
+                              ld_lds_tr8(ds_s + ds_tr[kc & 1][1] + dso));
+        const bf16x8 b = cat8(ld_lds_tr8(k_s + k_tr[0] + ko), ld_lds_tr8(k_s + k_tr[1] + ko));
         acc = mfma32x32x16(a, b, acc);
       }
+      if (dq_kh == 1) {
+        float* pp = part_s + dq_blk * 1024 + lane;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) pp[64 * x] = acc[x];
+      }
     }
-    // acc[x] = dQ[q = q0 + 8(x/4) + 4 half + x%4][d = 32 wave + l32]
-    float* dq_base = p.dq_acc + (long)it.seq_start * q_row + (long)h * D + wave * 32 + l32;
+    lds_barrier();  // partial sums of the second key half are in LDS
+    if (dq_issuer) {
+      const float* pp = part_s + dq_blk * 1024 + lane;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[x] += pp[64 * x];
+    }
+    // acc[x] = dQ[q = q0 + 8(x/4) + 4 half + x%4][d = 32 dq_blk + l32]
+    float* dq_base = p.dq_acc + (long)it.seq_start * q_row + (long)h * D + dq_blk * 32 + l32;
     if (!DET) {
-      if (wave < DQW) {
+      if (dq_issuer) {
+        // exactly 16 atomic instructions per issuing wave (rows past the end
+        // add 0 to the last row), so the next item can wait for its copies alone
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int q = q0 + 8 * (x >> 2) + 4 * half + (x & 3);
-          if (q < it.seq_len)
-            __hip_atomic_fetch_add(dq_base + (long)q * q_row, acc[x], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(dq_base + (long)min(q, last) * q_row,
+                                 q < it.seq_len ? acc[x] : 0.f, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     } else {
@@ -326,7 +379,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
       }
       __syncthreads();
-      if (wave < DQW) {
+      if (dq_issuer) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int q = q0 + 8 * (x >> 2) + 4 * half + (x & 3);
@@ -342,19 +395,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
-  // two-stage pipeline over the work items, unrolled so each LDS buffer is
-  // named statically: item t+1's rows are copied while item t is computed
+  // Before an item is computed its copies must have landed.  Only the
+  // previous item's dQ atomics (16 per issuing wave, fast mode) were issued
+  // after them, so those stay in flight.
+  auto wait_copies = [&](int item) {
+    if (!DET && item > 0 && dq_issuer) wait_vmem_leave16();
+    else wait_vmem();
+    lds_barrier();  // every wave's copies landed; the buffer being refilled is free
+  };
+  // two-stage pipeline over the work items: item t+1's rows are copied into
+  // the other buffer while item t is computed
   if (nitems > 0) issue_item(0, q_s0, do_s0, st_s0);
-  for (int item = 0; item < nitems; item += 2) {
-    wait_vmem();
-    __syncthreads();  // item landed; every wave is past the previous item's reads
-    if (item + 1 < nitems) issue_item(item + 1, q_s1, do_s1, st_s1);
-    compute_item(item, q_s0, do_s0, st_s0);
-    if (item + 1 >= nitems) break;
-    wait_vmem();
-    __syncthreads();
-    if (item + 2 < nitems) issue_item(item + 2, q_s0, do_s0, st_s0);
-    compute_item(item + 1, q_s1, do_s1, st_s1);
+  for (int item = 0; item < nitems; ++item) {
+    wait_copies(item);
+    const bool odd = item & 1;
+    char* qs = odd ? q_s1 : q_s0;
+    char* dos = odd ? do_s1 : do_s0;
+    char* sts = odd ? st_s1 : st_s0;
+    if (item + 1 < nitems) issue_item(item + 1, odd ? q_s0 : q_s1, odd ? do_s0 : do_s1,
+                                      odd ? st_s0 : st_s1);
+    compute_item(item, qs, dos, sts);
   }
 
   // ---------------- dK = scale * sum dS^T Q, dV = sum P^T dO for this wave's keys

@@ -125,17 +125,50 @@ struct PadTile {
   __device__ static constexpr int off(int row, int col) { return row * kPitch + col * 2; }
 };
 
+// Row-padded tile whose 16-byte chunks are also permuted within each group of
+// four by the row's quad index: chunk c of row r sits at physical chunk
+// c ^ ((r >> 2) & 3).  With a pitch of 16 (mod 64) dwords this keeps both
+// 16-byte operand reads of 16 consecutive rows and 8-byte transposed reads of
+// 4 consecutive rows x 64 bytes free of LDS bank conflicts, and every read
+// address stays one of two per-lane bases plus compile-time offsets.
+template <int ROWS, int CH, int STRIDE>
+struct SwzTile {
+  static_assert(CH % 4 == 0 && STRIDE >= CH, "tile geometry");
+  static constexpr int kPitch = STRIDE * 16;
+  static constexpr int kSlots = ROWS * STRIDE;
+  static constexpr int kBytes = kSlots * 16;
+  static constexpr int kInstr = (kSlots + 63) / 64;
+  __device__ static constexpr int phys(int r, int c) { return c ^ ((r >> 2) & 3); }
+  // byte offset of element `col` (a multiple of 4) of row r
+  __device__ static constexpr int off(int r, int col) {
+    return r * kPitch + (phys(r, col >> 3) << 4) + (col & 7) * 2;
+  }
+  // logical chunk stored in physical slot s (or -1 for a padding slot)
+  __device__ static constexpr int slot_chunk(int r, int pc) { return pc < CH ? phys(r, pc) : -1; }
+};
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 // One wave-wide direct load: lane l copies 16 bytes from gsrc into
 // lds_wave_base + 16*l (lds_wave_base must be the same for the whole wave).
+// Issued as inline assembly so that the compiler does not guard every later
+// LDS read with a wait for it: the kernels wait for these copies explicitly
+// (wait_vmem*) before the barrier that publishes the tile.  A vector-memory
+// instruction unknown to the compiler can only make its own waits stricter.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(m0) : "memory", "m0");
 }
 // Same with 4 bytes per lane (lds_wave_base + 4*l).
 __device__ __forceinline__ void dma4(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)gsrc, (lds_void_t*)lds_wave_base, 4, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gsrc), "s"(m0) : "memory", "m0");
 }
 
 // Direct copy of a padded tile (see PadTile): row r of the tile comes from
@@ -159,7 +192,47 @@ __device__ __forceinline__ void dma_tile(char* dst, const __bf16* src, long src_
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14); the builtin form lets the compiler's own wait insertion
+// know what has completed.
+constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
+constexpr int kWaitVm16 = 0x4F70;  // vmcnt(16)
+// Direct copy of a SwzTile (rows as in dma_tile).
+template <class T, int STRIDE, int NW>
+__device__ __forceinline__ void dma_swz_tile(char* dst, const __bf16* src, long src_row, int row0,
+                                             int last, int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < (T::kInstr + NW - 1) / NW; ++k) {
+    const int kk = k * NW + wave;
+    if (kk < T::kInstr) {
+      const int s = kk * 64 + lane;
+      if (s < T::kSlots) {
+        const int row = s / STRIDE;
+        int c = T::slot_chunk(row, s - row * STRIDE);
+        if (c < 0) c = 0;
+        dma16(src + (long)min(row0 + row, last) * src_row + c * 8, dst + kk * 1024);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  asm volatile("" ::: "memory");
+}
+// Wait until at most 16 vector-memory instructions of this wave are
+// outstanding (they retire in issue order, so everything older is complete).
+__device__ __forceinline__ void wait_vmem_leave16() {
+  __builtin_amdgcn_s_waitcnt(kWaitVm16);
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are
+// complete, global memory operations may stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i receives element i%4 of the 8-byte rows that lanes i/4,
