@@ -9,8 +9,9 @@ Prints one JSON line.  Besides the headline it carries:
   roofline      the dominant kernel (the backward main kernel): algorithmic
                 FLOPs per launch / its average duration from HIP events recorded
                 on its own stream during the timed steps, against the dense bf16
-                MFMA peak; `traffic` is filled from rocprofv3 counters when given
-                with --traffic-file;
+                MFMA peak; `traffic` is the kernel's HBM bytes per launch from
+                the recorded rocprofv3 counter runs (profiles/), or null when
+                the kernel sources changed since they were taken;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample (whole query
                 heads of the same workload) on this host's cores, scaled to the
                 metric's unit.
@@ -36,6 +37,34 @@ METRIC = "attention fwd+bwd TFLOPs/s (bf16, d=128, causal N=8K) and % of MFMA pe
 def flops(B, N, H, d, causal):
     f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
     return f, 2.5 * f
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.txt")
+KERNEL_SOURCES = ("fa_bwd.hip", "fa_common.h", "fa_launch.h")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the backward main kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_80_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path: str, config: dict):
+    """HBM bytes per launch of the backward main kernel from the recorded
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (each scaled by its copy-kernel
+    calibration factor), or None when the record is missing, was taken on
+    another workload, or the kernel sources changed since it was taken."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != kernel_source_hash() or rec.get("config") != config:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def make_inputs(B, N, Hq, Hkv, d, seed=0):
@@ -100,8 +129,8 @@ def main():
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
-    ap.add_argument("--traffic-file", default="",
-                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--traffic-file", default=TRAFFIC_FILE,
+                    help="recorded HBM bytes per launch of the dominant kernel")
     ap.add_argument("--extra", action="store_true",
                     help="also time the deterministic backward (reported as extras)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -163,10 +192,9 @@ def main():
     avg_bwd_ms = ms_bwd / max(1, n_bwd)
     avg_fwd_ms = ms_fwd / max(1, n_fwd)
     achieved = f_bwd / (avg_bwd_ms * 1e-3) / 1e12
-    traffic = None
-    if args.traffic_file and os.path.exists(args.traffic_file):
-        with open(args.traffic_file) as fh:
-            traffic = json.load(fh).get("bwd_main_bytes_per_launch")
+    traffic = measured_traffic(args.traffic_file,
+                               {"B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
+                                "deterministic": det})
 
     extras = {
         "fwd_kernel_ms": avg_fwd_ms,

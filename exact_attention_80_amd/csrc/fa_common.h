@@ -197,6 +197,99 @@ __device__ __forceinline__ void dma_tile(char* dst, const __bf16* src, long src_
 // know what has completed.
 constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
 constexpr int kWaitVm16 = 0x4F70;  // vmcnt(16)
+// ---------------------------------------------------------------------------
+// Buffer-descriptor copies.  A raw buffer descriptor (base, byte range) lives
+// in scalar registers; each lane supplies only a 32-bit byte offset, and
+// lanes whose offset falls outside the range read zeros.  Tiles are copied
+// with a descriptor whose base is the tile's first row and whose range ends
+// after the sequence's last valid row, so rows past the end arrive as zeros
+// without any clamping.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);  // stride 0: raw byte addressing
+  r[2] = (int)num_bytes;
+  r[3] = 0x00020000;                            // gfx9 data format word
+  return r;
+}
+
+// lane l copies 16 (or 4) bytes at byte `voff` of the buffer into
+// lds_wave_base + 16*l (4*l).
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t voff, void* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_buf(i32x4 rsrc, uint32_t voff, void* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// Byte range of a tile that starts at row `row0` of a sequence of `len` rows
+// of `row_bytes` pitch, `data_bytes` used per row (0 when the tile is empty).
+__device__ __forceinline__ uint32_t tile_range(int row0, int len, long row_bytes, int data_bytes) {
+  return row0 < len ? (uint32_t)((long)(len - 1 - row0) * row_bytes + data_bytes) : 0u;
+}
+
+// Per-lane offsets of the uniform-count copy of one tile (see dma_count):
+// computed once, reused for every tile of the same geometry.
+template <class T, int NW>
+struct TileCopy {
+  static constexpr int kN = (T::kInstr + NW - 1) / NW;
+  static constexpr int kLastLanes = T::kSlots - (T::kInstr - 1) * 64;  // lanes used by the last
+  uint32_t voff[kN];
+  int wave_, lane_;
+  template <class ChunkOf>
+  __device__ __forceinline__ void init(long row_bytes, int stride, int wave, int lane,
+                                       ChunkOf chunk_of) {
+    wave_ = wave;
+    lane_ = lane;
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int s = min(k * NW + wave, T::kInstr - 1) * 64 + lane;
+      const int row = s / stride;
+      int c = chunk_of(row, s - row * stride);
+      if (c < 0) c = 0;
+      voff[k] = (uint32_t)(row * row_bytes + c * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(char* dst, i32x4 rsrc) const {
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int kk = min(k * NW + wave_, T::kInstr - 1);  // wave-uniform
+      if (kk < T::kInstr - 1 || lane_ < kLastLanes) dma16_buf(rsrc, voff[k], dst + kk * 1024);
+    }
+  }
+};
+
+// Number of wave-wide copy instructions every wave issues for one tile when
+// the uniform variants below are used (the last instruction is repeated by
+// waves that have nothing left, rewriting identical bytes), so that a wave can
+// wait for "all but the newest n tiles" with one s_waitcnt vmcnt(n * count).
+template <class T, int NW>
+constexpr int dma_count() { return (T::kInstr + NW - 1) / NW; }
+
+template <class T, int NW, class ChunkOf>
+__device__ __forceinline__ void dma_uniform(char* dst, const __bf16* src, long src_row, int row0,
+                                            int last, int wave, int lane, int stride,
+                                            ChunkOf chunk_of) {
+#pragma unroll
+  for (int k = 0; k < dma_count<T, NW>(); ++k) {
+    const int kk = min(k * NW + wave, T::kInstr - 1);
+    const int s = kk * 64 + lane;
+    if (s < T::kSlots) {
+      const int row = s / stride;
+      int c = chunk_of(row, s - row * stride);
+      if (c < 0) c = 0;
+      dma16(src + (long)min(row0 + row, last) * src_row + c * 8, dst + kk * 1024);
+    }
+  }
+}
+
 // Direct copy of a SwzTile (rows as in dma_tile).
 template <class T, int STRIDE, int NW>
 __device__ __forceinline__ void dma_swz_tile(char* dst, const __bf16* src, long src_row, int row0,
@@ -222,6 +315,12 @@ __device__ __forceinline__ void wait_vmem() {
 }
 // Wait until at most 16 vector-memory instructions of this wave are
 // outstanding (they retire in issue order, so everything older is complete).
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void wait_vmem_leave16() {
   __builtin_amdgcn_s_waitcnt(kWaitVm16);
   asm volatile("" ::: "memory");

@@ -6,8 +6,8 @@
 //  * split-Q: wave w owns query rows 32w..32w+31 of the tile and sees every
 //    key/value tile, so no reduction between waves is ever needed;
 //  * K and V tiles of 64 keys are copied global->LDS by direct loads (no
-//    register staging) into row-padded tiles, double buffered: tile j+1 is in
-//    flight while tile j is computed;
+//    register staging) into padded tiles, through a ring of kFwdStages
+//    buffers: the next tiles are in flight while tile j is computed;
 //  * the score tile is computed transposed, S^T = K Q^T, so each lane holds one
 //    query column: the row max and row sum are in-lane plus one exchange
 //    between lane halves;
@@ -88,12 +88,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   constexpr int BR = NW * 32;
   constexpr int CH = D / 8;                      // 16-byte chunks per key row
   using KT = PadTile<kBC, CH, CH + 1>;           // K: 16-byte operand reads
-  using VT = PadTile<kBC, CH, CH + 2>;           // V: 8-byte transposed reads
+  using VT = SwzTile<kBC, CH, D == 128 ? 20 : 12>;  // V: 8-byte transposed reads
 
-  __shared__ __attribute__((aligned(16))) char k0[KT::kBytes];
-  __shared__ __attribute__((aligned(16))) char k1[KT::kBytes];
-  __shared__ __attribute__((aligned(16))) char v0[VT::kBytes];
-  __shared__ __attribute__((aligned(16))) char v1[VT::kBytes];
+  constexpr int STAGES = kFwdStages;             // K/V tiles in flight or in use
+  __shared__ __attribute__((aligned(16))) char kv_s[STAGES][KT::kBytes + VT::kBytes];
 
   const WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
   if (!wi.valid) return;
@@ -130,11 +128,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int kv_end = CAUSAL ? min(wi.seq_len, q0 + BR) : wi.seq_len;
   const int nt = (kv_end + kBC - 1) / kBC;
 
-  // ---- direct global->LDS copy of one K and one V tile (rows past the
-  // sequence end repeat the last valid row; their scores are masked)
-  auto issue_tile = [&](int j, char* kt, char* vt) {
-    dma_tile<KT, CH, CH + 1, NW>(kt, kbase, kv_row, j * kBC, wi.seq_len - 1, wave, lane);
-    dma_tile<VT, CH, CH + 2, NW>(vt, vbase, kv_row, j * kBC, wi.seq_len - 1, wave, lane);
+  // ---- direct global->LDS copy of one K and one V tile.  Rows past the
+  // sequence end arrive as zeros (buffer range check); their scores are
+  // masked.  Every wave issues the same number of copies per tile (kCopies).
+  constexpr int VST = D == 128 ? 20 : 12;
+  constexpr int kCopies = dma_count<KT, NW>() + dma_count<VT, NW>();
+  const long kv_bytes = kv_row * 2;
+  TileCopy<KT, NW> kcopy;
+  TileCopy<VT, NW> vcopy;
+  kcopy.init(kv_bytes, CH + 1, wave, lane, [](int, int pc) { return pc < CH ? pc : -1; });
+  vcopy.init(kv_bytes, VST, wave, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
+  auto issue_tile = [&](int j) {
+    char* kt = kv_s[j % STAGES];
+    const uint32_t range = tile_range(j * kBC, wi.seq_len, kv_bytes, D * 2);
+    kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * kv_row, range));
+    vcopy.issue(kt + KT::kBytes, make_rsrc(vbase + (long)j * kBC * kv_row, range));
   };
 
   // ---- running softmax state (per lane = per query; both lane halves agree)
@@ -146,10 +154,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   float m_ref = -INFINITY;  // reference max in scaled log2 units
   float lsum = 0.f;         // this lane half's partial row sum
 
+  // transposed reads of V rows 16kc + 8ld + 4(g16/2) + L16/4, columns
+  // 32db + 16(g16%2) + 4(L16%4): v_tr[ld] + 16 kc pitch + 64 db
+  const int v_tr[2] = {VT::off(4 * (g16 >> 1) + (L16 >> 2), 16 * (g16 & 1) + 4 * (L16 & 3)),
+                       VT::off(8 + 4 * (g16 >> 1) + (L16 >> 2), 16 * (g16 & 1) + 4 * (L16 & 3))};
+
   auto compute_tile = [&](int j, const char* kt, const char* vt) {
     const int key0 = j * kBC;
-    const bool active = !CAUSAL || key0 <= wq0 + 31;
-    if (!active) return;
     // S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
@@ -208,29 +219,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const bf16x8 pb = frag_rows(s[kc >> 1], kc & 1);
-      const int row0 = kc * 16 + 4 * (g16 >> 1) + (L16 >> 2);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int col = db * 32 + 16 * (g16 & 1) + 4 * (L16 & 3);
-        const u32x2 lo = ld_lds_tr8(vt + VT::off(row0, col));
-        const u32x2 hi = ld_lds_tr8(vt + VT::off(row0 + 8, col));
+        const int vo = 16 * kc * VT::kPitch + 64 * db;
+        const u32x2 lo = ld_lds_tr8(vt + v_tr[0] + vo);
+        const u32x2 hi = ld_lds_tr8(vt + v_tr[1] + vo);
         oacc[db] = mfma32x32x16(cat8(lo, hi), pb, oacc[db]);
       }
     }
   };
 
-  // two-stage pipeline, unrolled so each LDS buffer is named statically
-  if (nt > 0) issue_tile(0, k0, v0);
-  for (int j = 0; j < nt; j += 2) {
-    wait_vmem();
-    __syncthreads();  // tile j landed for every wave; tile j-1's buffers are free
-    if (j + 1 < nt) issue_tile(j + 1, k1, v1);
-    compute_tile(j, k0, v0);
-    if (j + 1 >= nt) break;
-    wait_vmem();
-    __syncthreads();
-    if (j + 2 < nt) issue_tile(j + 2, k0, v0);
-    compute_tile(j + 1, k1, v1);
+  // STAGES-deep copy ring: tiles j+1 .. j+STAGES-1 are in flight while tile j
+  // is computed.  Copies retire in issue order, so waiting until at most
+  // (tiles issued after j) x kCopies copies are outstanding means tile j is in.
+  wait_vmem();  // Q fragments
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < nt) issue_tile(t);
+  for (int j = 0; j < nt; ++j) {
+    const int newer = min(nt - 1 - j, STAGES - 2);  // tiles issued after j
+    if (newer >= 2) wait_vmem_leave<2 * kCopies>();
+    else if (newer == 1) wait_vmem_leave<kCopies>();
+    else wait_vmem();
+    lds_barrier();  // tile j landed for every wave; tile j-1's buffer is free
+    if (j + STAGES - 1 < nt) issue_tile(j + STAGES - 1);
+    const char* kt = kv_s[j % STAGES];
+    compute_tile(j, kt, kt + KT::kBytes);
   }
 
   // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2

@@ -8,6 +8,7 @@
 namespace fa {
 
 constexpr int kFwdWaves = 8;   // forward workgroup: 8 waves, 256 query rows
+constexpr int kFwdStages = 4;  // forward K/V copy ring depth (tiles)
 constexpr int kBwdWaves = 8;   // backward workgroup: 8 waves, 256 keys
 constexpr int kBwdBQ = 32;     // backward query tile
 constexpr int kBwdBC = kBwdWaves * 32;

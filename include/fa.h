@@ -20,9 +20,10 @@
  * ---------------------------------------
  *  - Tensors are caller-owned DEVICE memory (e.g. PyTorch allocations), dense,
  *    contiguous, 16-byte aligned.  Q, K, V, O, dO, dQ, dK, dV are bf16.
- *    The library never allocates or frees device memory and keeps no state
- *    beyond a per-device property cache, so calls on different streams are
- *    independent as long as their buffers (including workspaces) differ.
+ *    The library never allocates or frees device memory.  Its only host state
+ *    is a per-device property cache and the opt-in timing event pool below,
+ *    so calls on different streams are independent as long as their buffers
+ *    (including workspaces) differ.
  *  - Dense layout (token-major): Q/O/dO/dQ are [B, N, Hq, d]; K/V/dK/dV are
  *    [B, N, Hkv, d]; the logsumexp LSE is fp32 [B, Hq, N].
  *  - Packed variable-length layout: Q/O/dO/dQ are [T, Hq, d], K/V/dK/dV are
@@ -124,8 +125,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* ---- packed variable-length forward / backward ---------------------------- */
 
-/* max_seqlen: an upper bound on any sequence length, or 0 if unknown; it is only
- * checked on the device.  total_tokens = T = cu_seqlens[nseq]. */
+/* max_seqlen: a hint (an upper bound on any sequence length, or 0 if unknown);
+ * it must be >= 0 and is otherwise unused, since the scheduling kernel reads
+ * the lengths from cu_seqlens itself.  total_tokens = T = cu_seqlens[nseq]. */
 size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
                                     int causal);
 

@@ -10,6 +10,8 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_probs,
     head_forward_backward,
+    head_key_rows,
+    head_query_rows,
     head_probs,
     varlen_backward,
     varlen_forward,

@@ -214,6 +214,61 @@ def varlen_backward(q, k, v, do, cu_seqlens, scale: float, causal: bool,
     return dq, dk, dv
 
 
+def head_query_rows(qh, kh, vh, doh, scale: float, causal: bool, rows):
+    """O, LSE, D and dQ of chosen query rows of one head, for spot checks at
+    sizes where whole heads are too slow.
+
+    A query row needs nothing but its own scores: S_i = scale q_i K^T (causal:
+    keys j > i excluded), lse_i = m_i + ln sum_j exp(S_ij - m_i),
+    P_i = exp(S_i - lse_i), O_i = P_i V, D_i = dO_i . O_i, dP_i = dO_i V^T,
+    dS_i = P_i o (dP_i - D_i), dQ_i = scale dS_i K  ([FA2] "Problem and
+    motivation", "Core method" 1-2; the backward is the chain rule).
+    Returns (o [r,d], lse [r], dvec [r], dq [r,d]) in the order of `rows`.
+    """
+    qh, kh, vh, doh = _f64(qh), _f64(kh), _f64(vh), _f64(doh)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scale * (qh[rows] @ kh.T)
+    if causal:
+        s = np.where(np.arange(kh.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    m = s.max(axis=1)
+    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    p = np.exp(s - lse[:, None])
+    o = p @ vh
+    do_r = doh[rows]
+    dvec = (do_r * o).sum(axis=1)
+    ds = p * (do_r @ vh.T - dvec[:, None])
+    return o, lse, dvec, scale * (ds @ kh)
+
+
+def head_key_rows(qh, kh, vh, doh, scale: float, causal: bool, keys,
+                  row_chunk: int = ROW_CHUNK):
+    """dK and dV that one query head contributes to chosen keys of its
+    key/value head: dV_j = sum_i P_ij dO_i and dK_j = scale sum_i dS_ij q_i.
+
+    Only queries that see a chosen key contribute (causal: i >= min(keys)),
+    but each of them needs its whole score row for its logsumexp and for
+    D_i = dO_i . O_i; rows are taken in chunks of whole rows.  Summing the
+    results over the query heads of a group gives the group's dK, dV
+    ([FA2] "Core method" 4).  Returns (dk [r,d], dv [r,d]) in key order.
+    """
+    qh, kh, vh, doh = _f64(qh), _f64(kh), _f64(vh), _f64(doh)
+    keys = np.asarray(keys, dtype=np.int64)
+    n = qh.shape[0]
+    dk = np.zeros((keys.size, kh.shape[1]))
+    dv = np.zeros((keys.size, vh.shape[1]))
+    first = int(keys.min()) if causal and keys.size else 0
+    for r0 in range(first, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        q_c, do_c = qh[r0:r1], doh[r0:r1]
+        p, _ = head_probs(q_c, kh, scale, causal, r0)
+        d_c = (do_c * (p @ vh)).sum(axis=1)
+        p_k = p[:, keys]
+        ds_k = p_k * (do_c @ vh[keys].T - d_c[:, None])
+        dv += p_k.T @ do_c
+        dk += scale * (ds_k.T @ q_c)
+    return dk, dv
+
+
 def head_forward_backward(qh, kh, vh, doh, scale: float, causal: bool,
                           row_chunk: int = ROW_CHUNK):
     """One query head end to end (used to time the oracle on a sample of heads).

@@ -15,6 +15,22 @@ TOL_LSE = 1e-3
 TOL_GRAD = 2e-2
 
 
+def o_tolerance(ref: np.ndarray) -> np.ndarray:
+    """Per-element bound on |O - O*|: TOL_O wherever |O*| < 4.  From |O*| = 4 up,
+    the bf16 grid of the stored output is coarser than TOL_O (half an ulp is
+    2^-6 at 4), so the bound there is half a bf16 ulp of O* plus 2^-8 |O*|, the
+    worst case of rounding every probability to bf16 (relative 2^-9) before the
+    P V product."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.maximum(a, 1e-30)))
+    return np.where(a >= 4.0, np.maximum(TOL_O, 2.0 ** (e - 8) + a * 2.0 ** -8), TOL_O)
+
+
+def o_excess(o: np.ndarray, ref: np.ndarray) -> float:
+    """Largest |O - O*| / bound (<= 1 passes)."""
+    return float(np.max(np.abs(o - ref) / o_tolerance(ref))) if o.size else 0.0
+
+
 def to_dev(x: np.ndarray):
     import torch
     bits = inputs.bf16_bits(x).view(np.int16)

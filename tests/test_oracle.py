@@ -270,3 +270,51 @@ def test_flop_convention():
     f, b = ora.attention_flops(2, 8192, 16, 128, True)
     assert f == 4 * 2 * 16 * 8192 ** 2 * 128 / 2
     assert b == 2.5 * f
+
+
+def _torch_reference(q, k, v, do, scale, causal):
+    """torch CPU float64 explicit softmax + autograd on one head pair."""
+    import torch
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=(n != "do"))
+         for n, a in (("q", q), ("k", k), ("v", v), ("do", do))}
+    s = scale * t["q"] @ t["k"].T
+    if causal:
+        n = q.shape[0]
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    lse = torch.logsumexp(s, dim=1)
+    o = torch.softmax(s, dim=1) @ t["v"]
+    (o * t["do"]).sum().backward()
+    return (o.detach().numpy(), lse.detach().numpy(), t["q"].grad.numpy(),
+            t["k"].grad.numpy(), t["v"].grad.numpy())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_and_keys_match_autograd(causal):
+    """The spot-check routines (chosen query rows; chosen keys, summed over a
+    query-head group) against an independent torch float64 autograd."""
+    pytest.importorskip("torch")
+    x = inputs.dense_inputs(1, 150, 3, 1, 32, seed=11, round_bf16=False)
+    q, k, v, do = (x[n][0].astype(np.float64) for n in ("q", "k", "v", "do"))
+    scale = 0.17
+    rows = np.array([0, 1, 63, 64, 100, 149, 5])
+    keys = np.array([149, 0, 77, 3, 120])
+    dk_sum = np.zeros((keys.size, 32))
+    dv_sum = np.zeros((keys.size, 32))
+    for h in range(3):
+        ro, rlse, rdq, rdk, rdv = _torch_reference(q[:, h], k[:, 0], v[:, 0], do[:, h], scale,
+                                                   causal)
+        o, lse, dvec, dq = ora.head_query_rows(q[:, h], k[:, 0], v[:, 0], do[:, h], scale,
+                                               causal, rows)
+        assert np.max(np.abs(o - ro[rows])) <= 1e-12
+        assert np.max(np.abs(lse - rlse[rows])) <= 1e-12
+        assert np.max(np.abs(dvec - (ro[rows] * do[rows, h]).sum(axis=1))) <= 1e-12
+        assert np.max(np.abs(dq - rdq[rows])) <= 1e-12
+        dk, dv = ora.head_key_rows(q[:, h], k[:, 0], v[:, 0], do[:, h], scale, causal, keys,
+                                   row_chunk=7)
+        assert np.max(np.abs(dk - rdk[keys])) <= 1e-12
+        assert np.max(np.abs(dv - rdv[keys])) <= 1e-12
+        dk_sum += dk
+        dv_sum += dv
+    gq, gk, gv = ora.attention_backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    assert np.max(np.abs(dk_sum - gk[0, keys, 0])) <= 1e-12
+    assert np.max(np.abs(dv_sum - gv[0, keys, 0])) <= 1e-12
