@@ -62,7 +62,6 @@ struct BwdLds {
   static constexpr int statBytes = 2 * BQ * 4;       // LSE[BQ] then D[BQ]
   static constexpr int dsPitch = BQ * 2;             // dS^T row: 32 bf16
   static constexpr int dsBytes = BC * dsPitch;
-  static constexpr int partBytes = (NW / 2) * 64 * 16 * 4;
 };
 
 // byte offset of the 8-byte slot holding dS^T[key][4s .. 4s+3]
@@ -83,8 +82,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char do_s1[QT::kBytes];
   __shared__ __attribute__((aligned(16))) char st_s0[L::statBytes];
   __shared__ __attribute__((aligned(16))) char st_s1[L::statBytes];
-  __shared__ __attribute__((aligned(16))) char ds_s[L::dsBytes];
-  __shared__ __attribute__((aligned(16))) float part_s[L::partBytes / 4];
+  __shared__ __attribute__((aligned(16))) char ds_s0[L::dsBytes];
+  __shared__ __attribute__((aligned(16))) char ds_s1[L::dsBytes];
   __shared__ int sh_ticket;
 
   const int tid = threadIdx.x;
@@ -182,16 +181,19 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int nsteps = max(0, it.nq - i_start);
   const int nitems = GS * nsteps;
 
-  // direct copy of one query tile's Q, dO rows and LSE, D values
+  // direct copy of one query tile's Q, dO rows (rows past the sequence end
+  // read as zeros) and LSE, D values
+  TileCopy<QT, NW> qcopy;
+  qcopy.init(q_row * 2, ST, wave, lane, [](int row, int pc) { return QT::slot_chunk(row, pc); });
   auto issue_item = [&](int item, char* qd, char* dod, char* std_) {
     const int hh = item / nsteps;
     const int i = i_start + (item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
-    const bf16* qsrc = p.q + (long)it.seq_start * q_row + (long)h * D;
-    const bf16* dsrc = p.dout + (long)it.seq_start * q_row + (long)h * D;
-    dma_swz_tile<QT, ST, NW>(qd, qsrc, q_row, q0, last, wave, lane);
-    dma_swz_tile<QT, ST, NW>(dod, dsrc, q_row, q0, last, wave, lane);
+    const long tok = (long)it.seq_start + q0;
+    const uint32_t range = tile_range(q0, it.seq_len, q_row * 2, D * 2);
+    qcopy.issue(qd, make_rsrc(p.q + tok * q_row + (long)h * D, range));
+    qcopy.issue(dod, make_rsrc(p.dout + tok * q_row + (long)h * D, range));
     if (wave == NW - 1) {
       // lanes 0..31 copy the tile's LSE values, lanes 32..63 its D values;
       // both land at std_ + 4*lane, so the buffer holds LSE[BQ] then D[BQ]
@@ -204,12 +206,15 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
   };
 
-  // dQ work split: wave w owns dQ column block (w & 3) over key half (w >> 2)
-  constexpr int DQB = D / 32;                // 32-column blocks of dQ
-  const int dq_blk = wave & 3;
-  const int dq_kh = wave >> 2;
-  const bool dq_wave = dq_blk < DQB;
-  const bool dq_issuer = dq_wave && dq_kh == 0;  // issues the atomics
+  // dQ tile (BQ x D) of an item = dS (BQ x BC) K (BC x D) with 16x16x32
+  // products: wave w owns the 16-column block dblk of dQ for NQB 16-row
+  // blocks (both for d = 128, one for d = 64), over all BC keys, so no
+  // partial sums are exchanged and every wave adds its own block.
+  constexpr int DB16 = D / 16;               // 16-column blocks of dQ
+  constexpr int NQB = (2 * DB16) / NW;       // 16-row blocks per wave
+  static_assert(NQB >= 1 && NQB * NW == 2 * DB16, "dQ work split");
+  const int dblk = wave % DB16;
+  const int qb0 = (wave / DB16) * NQB;
 
   // Per-lane LDS byte offsets.  Every operand read below is one of these
   // bases plus a compile-time constant (the tile swizzle only permutes chunks
@@ -223,16 +228,110 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int rq = 4 * (g16 >> 1) + (L16 >> 2);
   const int cq = 16 * (g16 & 1) + 4 * (L16 & 3);
   const int q_tr[2] = {QT::off(rq, cq), QT::off(rq + 8, cq)};
-  //   dQ phase, keys 128 kh + 16kc + 8(g16/2) + 4ld + L16/4:
-  //   K columns 32 blk + cq:  base[ld] + 16 kc pitch
-  //   dS^T slots of queries cq:  base[kc & 1][ld] + 2048 (kc >> 1)
-  const int rk = dq_kh * (BC / 2) + 8 * (g16 >> 1) + (L16 >> 2);
-  const int k_tr[2] = {KT::off(rk, dq_blk * 32 + cq), KT::off(rk + 4, dq_blk * 32 + cq)};
-  const int qslot = 4 * (g16 & 1) + (L16 & 3);
-  const int ds_tr[2][2] = {{ds_off(rk, qslot), ds_off(rk + 4, qslot)},
-                           {ds_off(rk + 16, qslot), ds_off(rk + 20, qslot)}};
+  //   dQ products, keys 32ks + 8 g16 + 4ld + L16/4 (ks = 0 .. BC/32-1):
+  //   K columns 16 dblk + 4(L16%4):  k_tr[ld] + 32 ks pitch
+  //   dS^T slots of queries 16qb + 4(L16%4):  ds_tr[qb][ld] + 2048 ks
+  const int rk = 8 * g16 + (L16 >> 2);
+  const int k_tr[2] = {KT::off(rk, 16 * dblk + 4 * (L16 & 3)),
+                       KT::off(rk + 4, 16 * dblk + 4 * (L16 & 3))};
+  int ds_tr[NQB][2];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    ds_tr[qb][0] = ds_off(rk, 4 * (qb0 + qb) + (L16 & 3));
+    ds_tr[qb][1] = ds_off(rk + 4, 4 * (qb0 + qb) + (L16 & 3));
+  }
 
-  auto compute_item = [&](int item, const char* qs, const char* dos, const char* sts) {
+  // dQ of item `item` from its dS^T (all waves' rows), reduced into dq_acc
+  auto dq_item = [&](int item, const char* dss) {
+    const int hh = item / nsteps;
+    const int i = i_start + (item - hh * nsteps);
+    const int h = h0 + hh;
+    const int q0 = i * BQ;
+    f32x4 acc[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // operands of key step ks+1 are read while step ks's products run
+    bf16x8 ob[2], oa[2][NQB];
+    auto load_ks = [&](int ks, bf16x8& b, bf16x8 (&a)[NQB]) {
+      const int ko = 32 * ks * KT::kPitch;
+      b = cat8(ld_lds_tr8(k_s + k_tr[0] + ko), ld_lds_tr8(k_s + k_tr[1] + ko));
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        a[qb] = cat8(ld_lds_tr8(dss + ds_tr[qb][0] + 2048 * ks),
+                     ld_lds_tr8(dss + ds_tr[qb][1] + 2048 * ks));
+    };
+    load_ks(0, ob[0], oa[0]);
+#pragma unroll
+    for (int ks = 0; ks < BC / 32; ++ks) {
+      if (ks + 1 < BC / 32) load_ks(ks + 1, ob[(ks + 1) & 1], oa[(ks + 1) & 1]);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ks & 1][qb], ob[ks & 1], acc[qb],
+                                                          0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // acc[qb][r] = dQ[q = q0 + 16(qb0 + qb) + 4 g16 + r][d = 16 dblk + L16]
+    float* dq_base = p.dq_acc + (long)it.seq_start * q_row + (long)h * D + dblk * 16 + L16;
+    if (!DET) {
+      // exactly 4 NQB atomic instructions per wave (rows past the end add 0
+      // to the last row), so the next item can wait for its copies alone
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
+          __hip_atomic_fetch_add(dq_base + (long)min(q, last) * q_row,
+                                 q < it.seq_len ? acc[qb][r] : 0.f, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+      // ordered reduction: writers of a dQ tile apply in descending key-tile order
+      const int jhi = CAUSAL ? min(it.nkv - 1, (q0 + BQ - 1) / BC) : it.nkv - 1;
+      const int rank = jhi - it.jt;
+      long sidx;
+      if (VARLEN) sidx = (long)h * p.sem_slots + it.seq_start / BQ + it.seq + i;
+      else sidx = ((long)it.seq * p.Hq + h) * p.nq + i;
+      int* semp = p.sem + sidx;
+      // Wait for our turn.  The semaphore and the dQ accumulator are only ever
+      // touched by device-scope atomics, which are performed at the coherence
+      // point, so no cache invalidation or write-back is needed: the spin uses
+      // relaxed agent-scope loads and the adds below are issued after it.
+      if (tid == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        uint32_t polls = 0;
+        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != rank) {
+          __builtin_amdgcn_s_sleep(2);
+          if ((++polls & 63u) == 0) {
+            const uint32_t err = __hip_atomic_load(&p.hdr[kHdrErr], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            if ((err & kErrWaitTimeout) ||
+                __builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)p.spin_limit) {
+              __hip_atomic_fetch_or(&p.hdr[kHdrErr], kErrWaitTimeout, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
+          if (q < it.seq_len)
+            __hip_atomic_fetch_add(dq_base + (long)q * q_row, acc[qb][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+      // every add of this workgroup has been performed before the release
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  auto compute_item = [&](int item, const char* qs, const char* dos, const char* sts,
+                          char* dsd) {
     const int hh = item / nsteps;
     const int i = i_start + (item - hh * nsteps);
     const int h = h0 + hh;
@@ -299,109 +398,26 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         u32x2 w;
         w[0] = pack2_bf16(dp[4 * g + 0], dp[4 * g + 1]);
         w[1] = pack2_bf16(dp[4 * g + 2], dp[4 * g + 3]);
-        st_lds8(ds_s + ds_off(krow, 2 * g + half), w);
+        st_lds8(dsd + ds_off(krow, 2 * g + half), w);
       }
     } else {
       const int krow = wave * 32 + l32;
       const u32x2 z = {0u, 0u};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) st_lds8(ds_s + ds_off(krow, 2 * g + half), z);
-    }
-    lds_barrier();  // dS^T complete (dQ atomics of the previous item may still be in flight)
-
-    // ---------------- dQ_tile = dS K: block (dq_blk) over keys 128 dq_kh .. +127
-    f32x16 acc;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) acc[x] = 0.f;
-    if (dq_wave) {
-#pragma unroll
-      for (int kc = 0; kc < BC / 32; ++kc) {
-        const int dso = 2048 * (kc >> 1);
-        const int ko = 16 * kc * KT::kPitch;
-        const bf16x8 a = cat8(ld_lds_tr8(ds_s + ds_tr[kc & 1][0] + dso),
-                              ld_lds_tr8(ds_s + ds_tr[kc & 1][1] + dso));
-        const bf16x8 b = cat8(ld_lds_tr8(k_s + k_tr[0] + ko), ld_lds_tr8(k_s + k_tr[1] + ko));
-        acc = mfma32x32x16(a, b, acc);
-      }
-      if (dq_kh == 1) {
-        float* pp = part_s + dq_blk * 1024 + lane;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) pp[64 * x] = acc[x];
-      }
-    }
-    lds_barrier();  // partial sums of the second key half are in LDS
-    if (dq_issuer) {
-      const float* pp = part_s + dq_blk * 1024 + lane;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[x] += pp[64 * x];
-    }
-    // acc[x] = dQ[q = q0 + 8(x/4) + 4 half + x%4][d = 32 dq_blk + l32]
-    float* dq_base = p.dq_acc + (long)it.seq_start * q_row + (long)h * D + dq_blk * 32 + l32;
-    if (!DET) {
-      if (dq_issuer) {
-        // exactly 16 atomic instructions per issuing wave (rows past the end
-        // add 0 to the last row), so the next item can wait for its copies alone
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int q = q0 + 8 * (x >> 2) + 4 * half + (x & 3);
-          __hip_atomic_fetch_add(dq_base + (long)min(q, last) * q_row,
-                                 q < it.seq_len ? acc[x] : 0.f, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    } else {
-      // ordered reduction: writers of a dQ tile apply in descending key-tile order
-      const int jhi = CAUSAL ? min(it.nkv - 1, (q0 + BQ - 1) / BC) : it.nkv - 1;
-      const int rank = jhi - it.jt;
-      long sidx;
-      if (VARLEN) sidx = (long)h * p.sem_slots + it.seq_start / BQ + it.seq + i;
-      else sidx = ((long)it.seq * p.Hq + h) * p.nq + i;
-      int* semp = p.sem + sidx;
-      // Wait for our turn.  The semaphore and the dQ accumulator are only ever
-      // touched by device-scope atomics, which are performed at the coherence
-      // point, so no cache invalidation or write-back is needed: the spin uses
-      // relaxed agent-scope loads and the adds below are issued after it.
-      if (tid == 0) {
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        uint32_t polls = 0;
-        while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != rank) {
-          __builtin_amdgcn_s_sleep(2);
-          if ((++polls & 63u) == 0) {
-            const uint32_t err = __hip_atomic_load(&p.hdr[kHdrErr], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            if ((err & kErrWaitTimeout) ||
-                __builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)p.spin_limit) {
-              __hip_atomic_fetch_or(&p.hdr[kHdrErr], kErrWaitTimeout, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-          }
-        }
-      }
-      __syncthreads();
-      if (dq_issuer) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int q = q0 + 8 * (x >> 2) + 4 * half + (x & 3);
-          if (q < it.seq_len)
-            __hip_atomic_fetch_add(dq_base + (long)q * q_row, acc[x], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      // every add of this workgroup has been performed before the release
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int g = 0; g < 4; ++g) st_lds8(dsd + ds_off(krow, 2 * g + half), z);
     }
   };
 
-  // Before an item is computed its copies must have landed.  Only the
-  // previous item's dQ atomics (16 per issuing wave, fast mode) were issued
-  // after them, so those stay in flight.
+  // Per item: one barrier (the item's copies landed and the previous item's
+  // dS^T is complete), then the previous item's dQ products and atomics,
+  // then this item's S, dP, dV, dK and its dS^T (into the other buffer).
+  // Before an item is computed its copies must have landed; only the atomics
+  // of the dQ issued in the previous item (4 NQB per wave, fast mode) were
+  // issued after them, so those stay in flight.
   auto wait_copies = [&](int item) {
-    if (!DET && item > 0 && dq_issuer) wait_vmem_leave16();
+    if (!DET && item >= 2) wait_vmem_leave<4 * NQB>();
     else wait_vmem();
-    lds_barrier();  // every wave's copies landed; the buffer being refilled is free
+    lds_barrier();
   };
   // two-stage pipeline over the work items: item t+1's rows are copied into
   // the other buffer while item t is computed
@@ -414,7 +430,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     char* sts = odd ? st_s1 : st_s0;
     if (item + 1 < nitems) issue_item(item + 1, odd ? q_s0 : q_s1, odd ? do_s0 : do_s1,
                                       odd ? st_s0 : st_s1);
-    compute_item(item, qs, dos, sts);
+    if (item >= 1) dq_item(item - 1, odd ? ds_s0 : ds_s1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_item(item, qs, dos, sts, odd ? ds_s1 : ds_s0);
+  }
+  if (nitems > 0) {
+    lds_barrier();  // the last item's dS^T is complete
+    dq_item(nitems - 1, (nitems - 1) & 1 ? ds_s1 : ds_s0);
   }
 
   // ---------------- dK = scale * sum dS^T Q, dV = sum P^T dO for this wave's keys
