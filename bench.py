@@ -126,13 +126,14 @@ def main():
     ap.add_argument("--Hkv", type=int, default=0)
     ap.add_argument("--d", type=int, default=128)
     ap.add_argument("--non-causal", action="store_true")
-    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--dq-mode", type=int, default=0, choices=(0, 1, 2),
+                    help="dQ reduction: 0 fp32 atomics, 1 semaphore-ordered, 2 partial tiles")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
     ap.add_argument("--traffic-file", default=TRAFFIC_FILE,
                     help="recorded HBM bytes per launch of the dominant kernel")
     ap.add_argument("--extra", action="store_true",
-                    help="also time the deterministic backward (reported as extras)")
+                    help="also time the backward with the other dQ reduction modes (extras)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -159,7 +160,7 @@ def main():
     B, N, Hq, d = args.B, args.N, args.H, args.d
     Hkv = args.Hkv or Hq
     causal = not args.non_causal
-    det = args.deterministic
+    det = args.dq_mode
     scale = 1.0 / math.sqrt(d)
     torch.cuda.set_device(0)
     x = make_inputs(B, N, Hq, Hkv, d)
@@ -206,22 +207,27 @@ def main():
         "bwd_tflops": f_bwd / ((ms_bwd + ms_pre + ms_post) / max(1, n_bwd) * 1e-3) / 1e12,
         "pct_of_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
     }
-    if args.extra and not det:
-        wsd = fa.bwd_workspace(x["q"], x["k"], causal, True)
+    if args.extra:
         o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
-        for _ in range(3):
-            fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
-                   deterministic=True, workspace=wsd)
-        torch.cuda.synchronize()
-        fa.timing_begin()
-        for _ in range(args.steps):
-            fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
-                   deterministic=True, workspace=wsd)
-        kd = fa.timing_end()
-        det_ms = sum(kd[k][1] for k in ("bwd_pre", "bwd_main", "bwd_post")) / args.steps
-        fast_ms = (ms_bwd + ms_pre + ms_post) / max(1, n_bwd)
-        extras["det_bwd_tflops"] = f_bwd / (det_ms * 1e-3) / 1e12
-        extras["det_over_fast_speed"] = fast_ms / det_ms
+        this_ms = (ms_bwd + ms_pre + ms_post) / max(1, n_bwd)
+        for mode in (0, 1, 2):
+            if mode == det:
+                continue
+            wsd = fa.bwd_workspace(x["q"], x["k"], causal, mode)
+            for _ in range(3):
+                fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
+                       deterministic=mode, workspace=wsd)
+            torch.cuda.synchronize()
+            fa.timing_begin()
+            for _ in range(args.steps):
+                fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
+                       deterministic=mode, workspace=wsd)
+            kd = fa.timing_end()
+            del wsd
+            mode_ms = sum(kd[k][1] for k in ("bwd_pre", "bwd_main", "bwd_post")) / args.steps
+            extras[f"bwd_mode{mode}_ms"] = mode_ms
+            extras[f"bwd_mode{mode}_tflops"] = f_bwd / (mode_ms * 1e-3) / 1e12
+            extras[f"bwd_mode{mode}_over_this"] = this_ms / mode_ms
 
     line = {
         "metric": METRIC,
@@ -239,7 +245,7 @@ def main():
         "config": {
             "workload": f"{'causal' if causal else 'non-causal'} self-attention forward+backward, "
                         f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}, "
-                        f"{'deterministic' if det else 'atomic'} dQ reduction",
+                        f"{('atomic', 'semaphore-ordered', 'partial-tile')[det]} dQ reduction",
             "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
             "deterministic": det,
         },

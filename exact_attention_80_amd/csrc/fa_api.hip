@@ -172,7 +172,9 @@ FwdLayout fwd_layout(bool varlen, int nseq, long T) {
 }
 
 struct BwdLayout {
-  size_t hdr = 0, dvec = 0, dq_acc = 0, sem = 0, tiles = 0, dk_part = 0, dv_part = 0, total = 0;
+  size_t hdr = 0, dvec = 0, dq_acc = 0, dq_part = 0, sem = 0, tiles = 0, dk_part = 0,
+         dv_part = 0, total = 0;
+  long head_pairs = 0;  // mode 2: partial dQ tiles per (batch, query head)
   long sem_count = 0;
   int sem_slots = 0;  // varlen: per head
   int max_tiles = 0;
@@ -192,7 +194,7 @@ int choose_split(long units, int G) {
 }
 
 BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, int Hq, int Hkv, int d,
-                     int deterministic) {
+                     int deterministic, bool causal) {
   BwdLayout l;
   const int G = Hq / Hkv;
   long units;
@@ -207,8 +209,14 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, int Hq, int Hk
   l.dvec = off;
   off += align_up((size_t)T * Hq * 4);
   l.dq_acc = off;
-  off += align_up((size_t)T * Hq * d * 4);
-  if (deterministic) {
+  if (deterministic == 2) {
+    l.head_pairs = fa::bwd_partial_pairs(N, causal);
+    l.dq_part = off;
+    off += align_up((size_t)B * Hq * l.head_pairs * fa::kBwdBQ * d * 4);
+  } else {
+    off += align_up((size_t)T * Hq * d * 4);
+  }
+  if (deterministic == 1) {
     if (varlen) {
       l.sem_slots = (int)(T / fa::kBwdBQ + nseq + 1);
       l.sem_count = (long)Hq * l.sem_slots;
@@ -311,9 +319,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     return st;
   if (varlen && (st = check_ptr(cu, "cu_seqlens"))) return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
-  if (deterministic != 0 && deterministic != 1)
-    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0 or 1");
-  const BwdLayout lay = bwd_layout(varlen, B, N, nseq, T, Hq, Hkv, d, deterministic);
+  if (deterministic < 0 || deterministic > 2)
+    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1 or 2");
+  if (varlen && deterministic == 2)
+    return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 (partial-sum dQ) is dense-only");
+  const BwdLayout lay = bwd_layout(varlen, B, N, nseq, T, Hq, Hkv, d, deterministic, causal != 0);
   if (!ws || ws_bytes < lay.total)
     return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*bwd_workspace_size()");
   if ((st = check_ptr(ws, "ws"))) return st;
@@ -323,7 +333,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, 0));
   float* dvec = reinterpret_cast<float*>(at(ws, lay.dvec));
-  float* dq_acc = reinterpret_cast<float*>(at(ws, lay.dq_acc));
+  float* dq_acc = deterministic == 2 ? nullptr : reinterpret_cast<float*>(at(ws, lay.dq_acc));
   int* sem = reinterpret_cast<int*>(at(ws, lay.sem));
   long tk = timing_start(2, s);
   hipError_t e = fa::launch_bwd_pre(static_cast<const fa::bf16*>(o),
@@ -345,6 +355,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   p.dk_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dk_part)) : nullptr;
   p.dv_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dv_part)) : nullptr;
   p.sem = sem;
+  p.dq_part = deterministic == 2 ? reinterpret_cast<float*>(at(ws, lay.dq_part)) : nullptr;
+  p.head_pairs = lay.head_pairs;
   p.hdr = hdr;
   p.B = B;
   p.N = N;
@@ -377,14 +389,23 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   if (grid > 0) {
     tk = timing_start(1, s);
-    e = fa::launch_bwd(p, d, causal != 0, varlen, deterministic != 0, (int)grid, s);
+    e = fa::launch_bwd(p, d, causal != 0, varlen, deterministic, (int)grid, s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
   tk = timing_start(3, s);
-  e = fa::launch_bwd_post(dq_acc, static_cast<fa::bf16*>(dq), T * Hq * d, scale, p.dk_part,
-                          p.dv_part, static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
-                          T * Hkv * d, lay.S, s);
+  if (deterministic == 2) {
+    e = fa::launch_bwd_dq_reduce(p.dq_part, static_cast<fa::bf16*>(dq), B, N, Hq, d, causal != 0,
+                                 p.nq, p.nkv, lay.head_pairs, scale, s);
+    if (e == hipSuccess && lay.S > 1)
+      e = fa::launch_bwd_post(nullptr, nullptr, 0, scale, p.dk_part, p.dv_part,
+                              static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
+                              T * Hkv * d, lay.S, s);
+  } else {
+    e = fa::launch_bwd_post(dq_acc, static_cast<fa::bf16*>(dq), T * Hq * d, scale, p.dk_part,
+                            p.dv_part, static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
+                            T * Hkv * d, lay.S, s);
+  }
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward post launch");
   return FA_OK;
@@ -428,9 +449,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
-  (void)causal;
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
-  return bwd_layout(false, B, N, 0, (long)B * N, Hq, Hkv, d, deterministic != 0).total;
+  if (deterministic < 0 || deterministic > 2) return 0;
+  return bwd_layout(false, B, N, 0, (long)B * N, Hq, Hkv, d, deterministic, causal != 0).total;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -463,7 +484,8 @@ size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv,
                                     int causal, int deterministic) {
   (void)causal;
   if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
-  return bwd_layout(true, 0, 0, nseq, total_tokens, Hq, Hkv, d, deterministic != 0).total;
+  if (deterministic < 0 || deterministic > 1) return 0;
+  return bwd_layout(true, 0, 0, nseq, total_tokens, Hq, Hkv, d, deterministic, causal != 0).total;
 }
 
 int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -69,8 +69,25 @@ __device__ __forceinline__ int ds_off(int key, int s) {
   return key * (BQ * 2) + ((s ^ ((key >> 2) & 7)) << 3);
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool DET>
+// dQ reduction across key tiles
+constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
+constexpr int kDqOrdered = 1;  // semaphore-ordered adds into dq_acc (bit-reproducible)
+constexpr int kDqPartial = 2;  // plain stores of every partial tile, summed by bwd_dq_reduce
+
+// index of the partial dQ tile of (query tile i, key tile j) inside its
+// (sequence, head): the query tiles' key-tile counts laid end to end
+template <bool CAUSAL>
+__device__ __forceinline__ long pair_index(int i, int j, int nkv) {
+  if (CAUSAL) {  // query tile i meets key tiles 0 .. i / (BC / BQ)
+    const long a = i / (BC / BQ), r = i % (BC / BQ);
+    return (a + 1) * ((BC / BQ) / 2 * a + r) + j;
+  }
+  return (long)i * nkv + j;
+}
+
+template <int D, bool CAUSAL, bool VARLEN, int DQM>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+  constexpr bool DET = DQM == kDqOrdered;
   using L = BwdLds<D>;
   constexpr int ST = L::STRIDE;
   using KT = typename L::KT;
@@ -271,6 +288,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // acc[qb][r] = dQ[q = q0 + 16(qb0 + qb) + 4 g16 + r][d = 16 dblk + L16]
+    if (DQM == kDqPartial) {
+      // the tile in fragment order: 4 NQB floats per lane, NQB 16-byte stores
+      const long slot = ((long)it.seq * p.Hq + h) * p.head_pairs + pair_index<CAUSAL>(i, it.jt, it.nkv);
+      float* dst = p.dq_part + slot * (BQ * D) + ((wave * NQB) * 64 + lane) * 4;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) *reinterpret_cast<f32x4*>(dst + qb * 256) = acc[qb];
+      return;
+    }
     float* dq_base = p.dq_acc + (long)it.seq_start * q_row + (long)h * D + dblk * 16 + L16;
     if (!DET) {
       // exactly 4 NQB atomic instructions per wave (rows past the end add 0
@@ -412,10 +437,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // dS^T is complete), then the previous item's dQ products and atomics,
   // then this item's S, dP, dV, dK and its dS^T (into the other buffer).
   // Before an item is computed its copies must have landed; only the atomics
-  // of the dQ issued in the previous item (4 NQB per wave, fast mode) were
-  // issued after them, so those stay in flight.
+  // or stores of the dQ issued in the previous item (4 NQB or NQB per wave)
+  // were issued after them, so those stay in flight.
   auto wait_copies = [&](int item) {
-    if (!DET && item >= 2) wait_vmem_leave<4 * NQB>();
+    if (DQM == kDqAtomic && item >= 2) wait_vmem_leave<4 * NQB>();
+    else if (DQM == kDqPartial && item >= 2) wait_vmem_leave<NQB>();
     else wait_vmem();
     lds_barrier();
   };
@@ -460,25 +486,27 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool DET>
+template <int D, bool CAUSAL, bool VARLEN, int DQM>
 hipError_t launch_bwd_t(const BwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, VARLEN, DET>), dim3(grid), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, VARLEN, DQM>), dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
-hipError_t launch_bwd_det(const BwdParams& p, bool det, int grid, hipStream_t stream) {
-  return det ? launch_bwd_t<D, CAUSAL, VARLEN, true>(p, grid, stream)
-             : launch_bwd_t<D, CAUSAL, VARLEN, false>(p, grid, stream);
+hipError_t launch_bwd_mode(const BwdParams& p, int mode, int grid, hipStream_t stream) {
+  if (mode == kDqOrdered) return launch_bwd_t<D, CAUSAL, VARLEN, kDqOrdered>(p, grid, stream);
+  if (mode == kDqPartial && !VARLEN)
+    return launch_bwd_t<D, CAUSAL, false, kDqPartial>(p, grid, stream);
+  return launch_bwd_t<D, CAUSAL, VARLEN, kDqAtomic>(p, grid, stream);
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool varlen, bool det, int grid,
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool varlen, int mode, int grid,
                         hipStream_t stream) {
-  if (causal) return varlen ? launch_bwd_det<D, true, true>(p, det, grid, stream)
-                            : launch_bwd_det<D, true, false>(p, det, grid, stream);
-  return varlen ? launch_bwd_det<D, false, true>(p, det, grid, stream)
-                : launch_bwd_det<D, false, false>(p, det, grid, stream);
+  if (causal) return varlen ? launch_bwd_mode<D, true, true>(p, mode, grid, stream)
+                            : launch_bwd_mode<D, true, false>(p, mode, grid, stream);
+  return varlen ? launch_bwd_mode<D, false, true>(p, mode, grid, stream)
+                : launch_bwd_mode<D, false, false>(p, mode, grid, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -511,9 +539,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  if (dq_acc) {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < EPT; e += 4) *reinterpret_cast<f32x4*>(dq_acc + base + e) = z;
+    for (int e = 0; e < EPT; e += 4) *reinterpret_cast<f32x4*>(dq_acc + base + e) = z;
+  }
   if (sub == 0) {
     const int tok = row / Hq, h = row - tok * Hq;
     long idx;
@@ -558,12 +588,91 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const float* dq_acc, bf16
   }
 }
 
+// ---------------------------------------------------------------------------
+// partial-sum mode: dQ tile (b, h, i) = scale * sum over its key tiles j of the
+// partial tiles, added in ascending j (a fixed order), then stored as bf16.
+// One workgroup per query tile; the partial tiles are in the fragment order
+// of the dQ products (16x16 blocks: wave w owns columns 16 (w % (D/16)) ..
+// and row blocks NQB (w / (D/16)) .. of the tile).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* part, bf16* dq, int N,
+                                                            int Hq, int nq, int nkv,
+                                                            long head_pairs, float scale) {
+  constexpr int F = BQ * D;       // floats per tile
+  constexpr int V = F / 1024;     // float4 per thread
+  constexpr int DB16 = D / 16;
+  constexpr int NQB = (2 * DB16) / NW;
+  constexpr int PITCH = D + 4;    // LDS row pitch in floats
+  __shared__ float tile[BQ * PITCH];
+  const int t = threadIdx.x;
+  const int i = blockIdx.x % nq;
+  const int bh = blockIdx.x / nq;  // b * Hq + h
+  const int jn = CAUSAL ? i / (BC / BQ) + 1 : nkv;
+  const float* src = part + ((long)bh * head_pairs + pair_index<CAUSAL>(i, 0, nkv)) * F;
+  f32x4 acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < jn; ++j) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] += *reinterpret_cast<const f32x4*>(src + (long)j * F + 4 * (t + 256 * v));
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int f4 = t + 256 * v;          // (wave * NQB + qb) * 64 + lane
+    const int lane = f4 & 63, wq = f4 >> 6;
+    const int w = wq / NQB, qb = wq % NQB;
+    const int row0 = 16 * ((w / DB16) * NQB + qb) + 4 * (lane >> 4);
+    const int col = 16 * (w % DB16) + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tile[(row0 + r) * PITCH + col] = acc[v][r];
+  }
+  __syncthreads();
+  // thread t writes 16 consecutive elements (D = 128) or 8 (D = 64) of one row
+  constexpr int EPT = F / 256;
+  const int row = t / (D / EPT), c0 = (t % (D / EPT)) * EPT;
+  const int b = bh / Hq, h = bh % Hq;
+  const int q = i * BQ + row;
+  if (q >= N) return;
+  bf16* out = dq + (((long)b * N + q) * Hq + h) * D + c0;
+#pragma unroll
+  for (int e = 0; e < EPT; e += 8) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = pack2_bf16(tile[row * PITCH + c0 + e + 2 * k] * scale,
+                        tile[row * PITCH + c0 + e + 2 * k + 1] * scale);
+    *reinterpret_cast<u32x4*>(out + e) = w;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, bool det, int grid,
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int mode, int grid,
                       hipStream_t stream) {
-  if (d == 128) return launch_bwd_d<128>(p, causal, varlen, det, grid, stream);
-  return launch_bwd_d<64>(p, causal, varlen, det, grid, stream);
+  if (d == 128) return launch_bwd_d<128>(p, causal, varlen, mode, grid, stream);
+  return launch_bwd_d<64>(p, causal, varlen, mode, grid, stream);
+}
+
+hipError_t launch_bwd_dq_reduce(const float* part, bf16* dq, int B, int N, int Hq, int d,
+                                bool causal, int nq, int nkv, long head_pairs, float scale,
+                                hipStream_t stream) {
+  const long grid = (long)B * Hq * nq;
+  if (grid <= 0) return hipSuccess;
+  if (d == 128) {
+    if (causal) hipLaunchKernelGGL((bwd_dq_reduce_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+    else hipLaunchKernelGGL((bwd_dq_reduce_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+  } else {
+    if (causal) hipLaunchKernelGGL((bwd_dq_reduce_kernel<64, true>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+    else hipLaunchKernelGGL((bwd_dq_reduce_kernel<64, false>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+  }
+  return hipGetLastError();
+}
+
+long bwd_partial_pairs(int N, bool causal) {
+  const int nq = (N + kBwdBQ - 1) / kBwdBQ, nkv = (N + kBwdBC - 1) / kBwdBC;
+  if (!causal) return (long)nq * nkv;
+  const long a = nq / (kBwdBC / kBwdBQ), r = nq % (kBwdBC / kBwdBQ);
+  return (a + 1) * ((kBwdBC / kBwdBQ) / 2 * a + r);
 }
 
 hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, float* dvec, float* dq_acc, int* sem,
@@ -583,7 +692,8 @@ hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float s
                            const float* dk_part, const float* dv_part, bf16* dk, bf16* dv,
                            long kv_elems, int S, hipStream_t stream) {
   const long vec = dq_elems / 4;
-  const long blocks = min(4096L, max(1L, (vec + 255) / 256));
+  const long work = max(vec, S > 1 ? kv_elems / 4 : 0L);
+  const long blocks = min(4096L, max(1L, (work + 255) / 256));
   hipLaunchKernelGGL(bwd_post_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dq_acc, dq,
                      vec, scale, dk_part, dv_part, dk, dv, kv_elems / 4, S);
   return hipGetLastError();

@@ -405,7 +405,9 @@ struct BwdParams {
   bf16* dv;
   float* dk_part;         // [S, T, Hkv, d] fp32 when S > 1
   float* dv_part;
-  int* sem;               // dQ tile semaphores (deterministic mode)
+  int* sem;               // dQ tile semaphores (ordered mode)
+  float* dq_part;         // per-(query tile, key tile) dQ partial tiles (partial-sum mode)
+  long head_pairs;        // partial tiles per (sequence, query head)
   uint32_t* hdr;          // workspace header
   const int* cu_seqlens;  // varlen only
   const int* tiles;       // varlen only: (sequence, kv-tile) pairs in schedule order

@@ -25,8 +25,18 @@ hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, float* dvec, float* d
                           int* sem, long sem_count, uint32_t* hdr, int rows, int Hq, int d,
                           bool varlen, int N, int T, hipStream_t stream);
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, bool det, int grid,
+// mode: dQ reduction across key tiles (0 fp32 atomics, 1 semaphore-ordered
+// adds, 2 partial tiles summed by launch_bwd_dq_reduce; 2 is dense-only)
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int mode, int grid,
                       hipStream_t stream);
+
+// dQ = bf16(scale * sum of the partial tiles) for dense [B, N, Hq, d] (mode 2)
+hipError_t launch_bwd_dq_reduce(const float* part, bf16* dq, int B, int N, int Hq, int d,
+                                bool causal, int nq, int nkv, long head_pairs, float scale,
+                                hipStream_t stream);
+
+// partial dQ tiles per (batch, query head) in mode 2
+long bwd_partial_pairs(int N, bool causal);
 
 // dQ = bf16(scale * dQ_acc); when S > 1 also dK/dV = bf16(sum of the S partials).
 hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float scale,

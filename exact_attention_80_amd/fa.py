@@ -110,15 +110,19 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None):
     return o, lse
 
 
-def bwd_workspace(q, k, causal: bool, deterministic: bool) -> torch.Tensor:
+def bwd_workspace(q, k, causal: bool, deterministic: int | bool) -> torch.Tensor:
     B, N, Hq, d = q.shape
     n = _lib.fa_bwd_workspace_size(B, N, Hq, k.shape[2], d, int(causal), int(deterministic))
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None = None,
-        deterministic: bool = False, workspace: torch.Tensor | None = None):
-    """Dense backward -> (dq [B,N,Hq,d], dk [B,N,Hkv,d], dv [B,N,Hkv,d]) bf16."""
+        deterministic: int | bool = False, workspace: torch.Tensor | None = None):
+    """Dense backward -> (dq [B,N,Hq,d], dk [B,N,Hkv,d], dv [B,N,Hkv,d]) bf16.
+
+    deterministic selects the dQ reduction across key tiles: 0 (False) fp32
+    atomics, 1 (True) semaphore-ordered adds, 2 partial tiles summed in a fixed
+    order by a second kernel; 1 and 2 are bit-reproducible."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     _need(q, "q", (B, N, Hq, d))

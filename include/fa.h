@@ -101,8 +101,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* ---- dense backward ----------------------------------------------------- */
 
-/* Workspace bytes fa_bwd needs (fp32 dQ accumulator, D = rowsum(dO o O),
- * ordering semaphores, split dK/dV partials). */
+/* Workspace bytes fa_bwd needs (D = rowsum(dO o O), the fp32 dQ accumulator or,
+ * for deterministic == 2, the fp32 partial dQ tiles (32 x d floats per pair of
+ * a 32-row query tile and a 256-key tile that meet: about 2.2 GB for causal
+ * B=2, Hq=16, N=8192, d=128), ordering semaphores, split dK/dV partials).
+ * 0 when the sizes or the mode are invalid. */
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic);
 
@@ -114,8 +117,11 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
  * ([FA2] "Core method" 2 and 4).  Work is split over key/value tiles; the
  * partial dQ of every tile is reduced in fp32 with device atomics when
  * deterministic == 0 ([FA4B] 2.1), or in a fixed order serialised by
- * semaphores when deterministic == 1 ([FA4B] 3.2, 3.3.1), which makes
- * dQ/dK/dV bit-identical from run to run.  dK/dV never use atomics.
+ * semaphores when deterministic == 1 ([FA4B] 3.2, 3.3.1), or, when
+ * deterministic == 2, stored as one fp32 tile per (query tile, key tile)
+ * pair and summed in ascending key-tile order by a second kernel (no atomics;
+ * dense layout only).  Modes 1 and 2 make dQ/dK/dV bit-identical from run to
+ * run.  dK/dV never use atomics.  Any other value: FA_ERR_INVALID_ARG.
  * Outputs dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] bf16.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -145,7 +151,8 @@ int fa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* l
 size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
                                     int causal, int deterministic);
 
-/* Backward over a packed batch; semantics as fa_bwd, per sequence. */
+/* Backward over a packed batch; semantics as fa_bwd, per sequence.
+ * deterministic must be 0 or 1 (2 returns FA_ERR_UNSUPPORTED). */
 int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
@@ -170,7 +177,7 @@ int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* 
  * in milliseconds:
  *   kind 0: forward kernel;  kind 1: backward main kernel;
  *   kind 2: backward preprocess (D = rowsum(dO o O), zeroing);
- *   kind 3: backward post (dQ conversion, split dK/dV sum);
+ *   kind 3: backward post (dQ conversion or partial-tile sum, split dK/dV sum);
  *   kind 4: variable-length scheduler.
  * counts / ms must each point to FA_TIMING_KINDS elements (or be NULL).
  * Events are created lazily and reused; nothing is allocated on the device. */

@@ -90,7 +90,8 @@ def bwd(lib, ws=P, ws_bytes=None, det=0, d=64, dq=P, B=1, N=128, Hq=2, Hkv=2):
 def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws_bytes=16) == WORKSPACE
-    assert bwd(lib, det=2) == INVALID
+    assert bwd(lib, det=3) == INVALID
+    assert bwd(lib, det=-1) == INVALID
     assert bwd(lib, dq=None) == INVALID
     assert bwd(lib, d=80) == UNSUPPORTED
     assert bwd(lib, ws=MIS) == INVALID
@@ -103,6 +104,16 @@ def test_workspace_sizes(lib):
     det = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 1)
     assert fast >= B * N * Hq * d * 4 + B * N * Hq * 4  # fp32 dQ accumulator + D
     assert det > fast                                    # plus the semaphores
+    # partial-sum mode: one fp32 tile of 32 x d per (query tile, key tile) pair
+    # (causal: query tile i meets key tiles 0 .. i / 8), no dQ accumulator
+    nq = (N + 31) // 32
+    pairs = sum(i // 8 + 1 for i in range(nq))
+    part = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 2)
+    pairs_bytes = B * Hq * pairs * 32 * d * 4
+    assert abs((part - fast) - (pairs_bytes - B * N * Hq * d * 4)) <= 1024
+    full = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 0, 2)
+    assert full >= B * Hq * nq * ((N + 255) // 256) * 32 * d * 4
+    assert lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 3) == 0
     assert lib.fa_bwd_workspace_size(B, N, 3, 2, d, 1, 0) == 0
     vf = lib.fa_varlen_fwd_workspace_size(5, 4000, Hq, Hkv, d, 1)
     vb = lib.fa_varlen_bwd_workspace_size(5, 4000, Hq, Hkv, d, 1, 1)
@@ -121,6 +132,10 @@ def test_varlen_rejects_bad_arguments(lib):
                              None) == WORKSPACE
     assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 0, 0, 2, 2, 64, 0.1, 1, 1, P, wb,
                              None) == INVALID
+    # the partial-sum dQ reduction is dense-only
+    assert lib.fa_varlen_bwd_workspace_size(3, 300, 2, 2, 64, 1, 2) == 0
+    assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 2, P, wb,
+                             None) == UNSUPPORTED
 
 
 def test_workspace_error_rejects_null(lib):

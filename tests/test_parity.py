@@ -71,24 +71,39 @@ def test_dense_parity(fa, shape, causal):
     check_against_oracle(x, outs, causal, d)
 
 
+@pytest.mark.parametrize("mode", [1, 2], ids=["ordered", "partial"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_dense_parity_deterministic(fa, causal):
-    x, _, outs = run_dense(fa, 2, 451, 6, 2, 128, causal, seed=3, deterministic=True)
+def test_dense_parity_deterministic(fa, causal, mode):
+    x, _, outs = run_dense(fa, 2, 451, 6, 2, 128, causal, seed=3, deterministic=mode)
     check_against_oracle(x, outs, causal, 128)
 
 
+PARTIAL_CASES = [(1, 128, 2, 2, 64), (1, 1, 2, 1, 128), (1, 17, 3, 1, 64), (2, 300, 8, 2, 128),
+                 (1, 1024, 4, 2, 128), (1, 777, 2, 2, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", PARTIAL_CASES, ids=lambda s: "x".join(map(str, s)))
+def test_dense_parity_partial_sums(fa, shape, causal):
+    """dQ summed from per-(query tile, key tile) partial tiles (mode 2)."""
+    B, N, Hq, Hkv, d = shape
+    x, _, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=7, deterministic=2)
+    check_against_oracle(x, outs, causal, d)
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["ordered", "partial"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 513, 4, 2, 128), (1, 640, 2, 1, 64)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_deterministic_is_bit_identical(fa, shape, causal):
+def test_deterministic_is_bit_identical(fa, shape, causal, mode):
     import torch
     B, N, Hq, Hkv, d = shape
-    x, t, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=5, deterministic=True)
+    x, t, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=5, deterministic=mode)
     o, lse = outs[0], outs[1]
     ref = [a.clone() for a in outs[2:]]
     for rep in range(10):
         g = fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=causal,
-                   softmax_scale=scale_for(d), deterministic=True)
+                   softmax_scale=scale_for(d), deterministic=mode)
         for a, b in zip(g, ref):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rep
     o2, lse2 = fa.fwd(t["q"], t["k"], t["v"], causal=causal, softmax_scale=scale_for(d))
