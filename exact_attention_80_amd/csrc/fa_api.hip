@@ -172,7 +172,7 @@ FwdLayout fwd_layout(bool varlen, int nseq, long T) {
 }
 
 struct BwdLayout {
-  size_t hdr = 0, dvec = 0, dq_acc = 0, dq_part = 0, sem = 0, tiles = 0, dk_part = 0,
+  size_t hdr = 0, dvec = 0, lse2 = 0, dq_acc = 0, dq_part = 0, sem = 0, tiles = 0, dk_part = 0,
          dv_part = 0, total = 0;
   long head_pairs = 0;  // mode 2: partial dQ tiles per (batch, query head)
   long sem_count = 0;
@@ -207,6 +207,8 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, int Hq, int Hk
   l.S = choose_split(units, G);
   size_t off = align_up(fa::kHdrWords * 4);
   l.dvec = off;
+  off += align_up((size_t)T * Hq * 4);
+  l.lse2 = off;
   off += align_up((size_t)T * Hq * 4);
   l.dq_acc = off;
   if (deterministic == 2) {
@@ -336,9 +338,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   float* dq_acc = deterministic == 2 ? nullptr : reinterpret_cast<float*>(at(ws, lay.dq_acc));
   int* sem = reinterpret_cast<int*>(at(ws, lay.sem));
   long tk = timing_start(2, s);
+  float* lse2 = reinterpret_cast<float*>(at(ws, lay.lse2));
   hipError_t e = fa::launch_bwd_pre(static_cast<const fa::bf16*>(o),
-                                    static_cast<const fa::bf16*>(dout), dvec, dq_acc, sem,
-                                    lay.sem_count, hdr, (int)(T * Hq), Hq, d, varlen, N, (int)T, s);
+                                    static_cast<const fa::bf16*>(dout), lse, dvec, lse2, dq_acc,
+                                    sem, lay.sem_count, hdr, (int)(T * Hq), Hq, d, varlen, N,
+                                    (int)T, s);
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
 
@@ -347,7 +351,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   p.k = static_cast<const fa::bf16*>(k);
   p.v = static_cast<const fa::bf16*>(v);
   p.dout = static_cast<const fa::bf16*>(dout);
-  p.lse = lse;
+  p.lse = lse2;  // LSE * log2(e), written by the preprocess
   p.dvec = dvec;
   p.dq_acc = dq_acc;
   p.dk = static_cast<fa::bf16*>(dk);

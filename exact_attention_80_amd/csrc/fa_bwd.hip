@@ -22,6 +22,8 @@
 //    the causal walk (diagonal first) never stalls on its first write.
 //  * post: dQ = bf16(scale * dQ_acc); split subgroups' dK/dV partials are
 //    summed in a fixed order.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -34,16 +36,6 @@ constexpr int NT = NW * 64;
 constexpr int BQ = kBwdBQ;
 constexpr int BC = kBwdBC;
 
-struct BwdItem {
-  int seq;        // batch index (dense) or sequence index (varlen)
-  int seq_start;
-  int seq_len;
-  int hkv;
-  int split;      // query-head subgroup
-  int jt;         // key tile
-  int nq;         // query tiles of this sequence
-  int nkv;        // key tiles of this sequence
-};
 
 // LDS plan.  K, Q and dO tiles are row-major SwzTiles (pitch 16 mod 64
 // dwords) filled by direct global->LDS loads; Q/dO/LSE/D are double
@@ -67,22 +59,6 @@ struct BwdLds {
 // byte offset of the 8-byte slot holding dS^T[key][4s .. 4s+3]
 __device__ __forceinline__ int ds_off(int key, int s) {
   return key * (BQ * 2) + ((s ^ ((key >> 2) & 7)) << 3);
-}
-
-// dQ reduction across key tiles
-constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
-constexpr int kDqOrdered = 1;  // semaphore-ordered adds into dq_acc (bit-reproducible)
-constexpr int kDqPartial = 2;  // plain stores of every partial tile, summed by bwd_dq_reduce
-
-// index of the partial dQ tile of (query tile i, key tile j) inside its
-// (sequence, head): the query tiles' key-tile counts laid end to end
-template <bool CAUSAL>
-__device__ __forceinline__ long pair_index(int i, int j, int nkv) {
-  if (CAUSAL) {  // query tile i meets key tiles 0 .. i / (BC / BQ)
-    const long a = i / (BC / BQ), r = i % (BC / BQ);
-    return (a + 1) * ((BC / BQ) / 2 * a + r) + j;
-  }
-  return (long)i * nkv + j;
 }
 
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
@@ -382,47 +358,57 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       const float* dv_s = lse_s + BQ;
       const bool need_mask = (CAUSAL && q0 < wk0 + 31) || (wk0 + 32 > it.seq_len) ||
                              (q0 + BQ > it.seq_len);
+      // P = exp2(S c - LSE log2 e), dS = P o (dP - D); with a causal mask the
+      // masked copy runs on diagonal and ragged tiles only (a uniform branch)
+      auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * g + 4 * half);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_s + 8 * g + 4 * half);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * g + 4 * half);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_s + 8 * g + 4 * half);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = 4 * g + e;
-          float pr = fast_exp2(fmaf(s[x], p.c, -l4[e] * kLog2e));
-          if (need_mask) {
-            const int q = q0 + 8 * g + 4 * half + e;
-            if (!key_ok || q >= it.seq_len || (CAUSAL && mykey > q)) pr = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int x = 4 * g + e;
+            float pr = fast_exp2(fmaf(s[x], p.c, -l4[e]));
+            if (decltype(masked)::value) {
+              const int q = q0 + 8 * g + 4 * half + e;
+              if (!key_ok || q >= it.seq_len || (CAUSAL && mykey > q)) pr = 0.f;
+            }
+            s[x] = pr;
+            dp[x] = pr * (dp[x] - d4[e]);
           }
-          s[x] = pr;
-          dp[x] = pr * (dp[x] - d4[e]);
         }
+      };
+      if (CAUSAL && !need_mask) softmax_grad(std::false_type{});
+      else softmax_grad(std::true_type{});
+      bf16x8 pa[2], dsa[2];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        pa[qc] = frag_rows(s, qc);
+        dsa[qc] = frag_rows(dp, qc);
       }
       // dV += P^T dO and dK += dS^T Q over two 16-query chunks; the B operands
       // are transposed reads of the row-major dO / Q tiles, rows
       // 16qc + 8ld + 4half + 0..3 matching the registers of P and dS
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
-        const bf16x8 pa = frag_rows(s, qc);
-        const bf16x8 dsa = frag_rows(dp, qc);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 64 * db;
           const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 64 * db;
           const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
           const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
-          dv_acc[db] = mfma32x32x16(pa, bdo, dv_acc[db]);
-          dk_acc[db] = mfma32x32x16(dsa, bq, dk_acc[db]);
+          dv_acc[db] = mfma32x32x16(pa[qc], bdo, dv_acc[db]);
+          dk_acc[db] = mfma32x32x16(dsa[qc], bq, dk_acc[db]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // dS^T (bf16) rows of this wave's keys: 4 consecutive queries per store
+      // dS^T (bf16) rows of this wave's keys: the 4 consecutive queries of
+      // register group g are words 2(g%2), 2(g%2)+1 of dsa[g/2]
       const int krow = wave * 32 + l32;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack2_bf16(dp[4 * g + 0], dp[4 * g + 1]);
-        w[1] = pack2_bf16(dp[4 * g + 2], dp[4 * g + 3]);
+        const u32x4 w4 = as_u32x4(dsa[g >> 1]);
+        const u32x2 w = (g & 1) ? u32x2{w4[2], w4[3]} : u32x2{w4[0], w4[1]};
         st_lds8(dsd + ds_off(krow, 2 * g + half), w);
       }
     } else {
@@ -513,7 +499,8 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool varlen, int mode, 
 // preprocess: D = rowsum(dO o O); zero dQ_acc, semaphores, header
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16* dout, float* dvec,
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16* dout,
+                                                      const float* lse, float* dvec, float* lse2,
                                                       float* dq_acc, int* sem, long sem_count,
                                                       uint32_t* hdr, int rows, int Hq, bool varlen,
                                                       int N, int T) {
@@ -553,6 +540,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
       idx = ((long)b * Hq + h) * N + n;
     }
     dvec[idx] = acc;
+    lse2[idx] = lse[idx] * kLog2e;
   }
 }
 
@@ -653,17 +641,24 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int m
   return launch_bwd_d<64>(p, causal, varlen, mode, grid, stream);
 }
 
+template <int D, bool CAUSAL>
+void launch_reduce_t(const float* part, bf16* dq, int N, int Hq, int nq, int nkv,
+                     long head_pairs, float scale, long grid, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_reduce_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+}
+
 hipError_t launch_bwd_dq_reduce(const float* part, bf16* dq, int B, int N, int Hq, int d,
                                 bool causal, int nq, int nkv, long head_pairs, float scale,
                                 hipStream_t stream) {
   const long grid = (long)B * Hq * nq;
   if (grid <= 0) return hipSuccess;
   if (d == 128) {
-    if (causal) hipLaunchKernelGGL((bwd_dq_reduce_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
-    else hipLaunchKernelGGL((bwd_dq_reduce_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+    if (causal) launch_reduce_t<128, true>(part, dq, N, Hq, nq, nkv, head_pairs, scale, grid, stream);
+    else launch_reduce_t<128, false>(part, dq, N, Hq, nq, nkv, head_pairs, scale, grid, stream);
   } else {
-    if (causal) hipLaunchKernelGGL((bwd_dq_reduce_kernel<64, true>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
-    else hipLaunchKernelGGL((bwd_dq_reduce_kernel<64, false>), dim3((unsigned)grid), dim3(256), 0, stream, part, dq, N, Hq, nq, nkv, head_pairs, scale);
+    if (causal) launch_reduce_t<64, true>(part, dq, N, Hq, nq, nkv, head_pairs, scale, grid, stream);
+    else launch_reduce_t<64, false>(part, dq, N, Hq, nq, nkv, head_pairs, scale, grid, stream);
   }
   return hipGetLastError();
 }
@@ -675,16 +670,16 @@ long bwd_partial_pairs(int N, bool causal) {
   return (a + 1) * ((kBwdBC / kBwdBQ) / 2 * a + r);
 }
 
-hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, float* dvec, float* dq_acc, int* sem,
-                          long sem_count, uint32_t* hdr, int rows, int Hq, int d, bool varlen,
-                          int N, int T, hipStream_t stream) {
+hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, float* dvec,
+                          float* lse2, float* dq_acc, int* sem, long sem_count, uint32_t* hdr,
+                          int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream) {
   const int grid = max(1, (rows + 15) / 16);
   if (d == 128)
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, stream, o, dout, dvec,
-                       dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
+                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
   else
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid), dim3(256), 0, stream, o, dout, dvec,
-                       dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
+                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
   return hipGetLastError();
 }
 

@@ -393,12 +393,25 @@ struct FwdParams {
   float c;                // softmax_scale * log2(e)
 };
 
+// One backward work item: a key tile of one (sequence, key/value head,
+// query-head subgroup).
+struct BwdItem {
+  int seq;        // batch index (dense) or sequence index (varlen)
+  int seq_start;
+  int seq_len;
+  int hkv;
+  int split;      // query-head subgroup
+  int jt;         // key tile
+  int nq;         // query tiles of this sequence
+  int nkv;        // key tiles of this sequence
+};
+
 struct BwdParams {
   const bf16* q;
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* lse;
+  const float* lse;       // LSE * log2(e), laid out like the forward's logsumexp
   const float* dvec;      // D = rowsum(dO o O), laid out like lse
   float* dq_acc;          // [T, Hq, d] fp32
   bf16* dk;

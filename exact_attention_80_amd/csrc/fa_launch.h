@@ -13,17 +13,35 @@ constexpr int kBwdWaves = 8;   // backward workgroup: 8 waves, 256 keys
 constexpr int kBwdBQ = 32;     // backward query tile
 constexpr int kBwdBC = kBwdWaves * 32;
 
+// dQ reduction across key tiles
+constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
+constexpr int kDqOrdered = 1;  // semaphore-ordered adds into dq_acc (bit-reproducible)
+constexpr int kDqPartial = 2;  // plain stores of every partial tile, summed by bwd_dq_reduce
+
+// Index of the partial dQ tile of (query tile i, key tile j) inside its
+// (sequence, head): the query tiles' key-tile counts laid end to end (causal:
+// query tile i meets key tiles 0 .. i / (kBwdBC / kBwdBQ)).
+template <bool CAUSAL>
+__host__ __device__ __forceinline__ long pair_index(int i, int j, int nkv) {
+  constexpr int R = kBwdBC / kBwdBQ;
+  if (CAUSAL) {
+    const long a = i / R, r = i % R;
+    return (a + 1) * (R / 2 * a + r) + j;
+  }
+  return (long)i * nkv + j;
+}
+
 int fwd_tile_rows();
 int fwd_tile_keys();
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,
                       hipStream_t stream);
 
-// D = rowsum(dO o O) in the logsumexp layout; zeroes the fp32 dQ accumulator,
-// the semaphores and the workspace header.
-hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, float* dvec, float* dq_acc,
-                          int* sem, long sem_count, uint32_t* hdr, int rows, int Hq, int d,
-                          bool varlen, int N, int T, hipStream_t stream);
+// D = rowsum(dO o O) and LSE * log2(e) in the logsumexp layout; zeroes the
+// fp32 dQ accumulator (when given), the semaphores and the workspace header.
+hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, float* dvec,
+                          float* lse2, float* dq_acc, int* sem, long sem_count, uint32_t* hdr,
+                          int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream);
 
 // mode: dQ reduction across key tiles (0 fp32 atomics, 1 semaphore-ordered
 // adds, 2 partial tiles summed by launch_bwd_dq_reduce; 2 is dense-only)
