@@ -56,9 +56,15 @@ struct BwdLds {
   static constexpr int dsBytes = BC * dsPitch;
 };
 
-// byte offset of the 8-byte slot holding dS^T[key][4s .. 4s+3]
+// byte offset of the 8-byte slot holding dS^T[key][4s .. 4s+3].  The slot
+// is permuted by f(k) = k ^ ((k & 2) << 1) of the row's quad index k = (key/4)
+// mod 8: a bijection, so the stores of 32 consecutive keys to one slot hit 32
+// different 2-bank pairs, and the quads k and k ^ 2 read together by the two
+// 16-lane halves of a transposed read land in different 32-byte halves of
+// their rows.
 __device__ __forceinline__ int ds_off(int key, int s) {
-  return key * (BQ * 2) + ((s ^ ((key >> 2) & 7)) << 3);
+  const int k = (key >> 2) & 7;
+  return key * (BQ * 2) + ((s ^ k ^ ((k & 2) << 1)) << 3);
 }
 
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
