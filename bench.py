@@ -226,6 +226,8 @@ def main():
             del wsd
             mode_ms = sum(kd[k][1] for k in ("bwd_pre", "bwd_main", "bwd_post")) / args.steps
             extras[f"bwd_mode{mode}_ms"] = mode_ms
+            extras[f"bwd_mode{mode}_main_ms"] = kd["bwd_main"][1] / args.steps
+            extras[f"bwd_mode{mode}_post_ms"] = kd["bwd_post"][1] / args.steps
             extras[f"bwd_mode{mode}_tflops"] = f_bwd / (mode_ms * 1e-3) / 1e12
             extras[f"bwd_mode{mode}_over_this"] = this_ms / mode_ms
 
