@@ -14,7 +14,13 @@ Recipe:
     each l = floor(exp(U(ln lo, ln(hi+1)))) clipped to [lo, hi]; when fewer
     than lo tokens would remain the last length absorbs them (or leaves lo for
     one more sequence when the remainder exceeds hi), so every length is in
-    [lo, hi] and they sum exactly to the token total.
+    [lo, hi] and they sum exactly to the token total;
+  * separate query and key lengths (decode-shaped batches): key lengths as
+    above; then, from Generator(PCG64(query_seed)), per sequence in order a
+    uniform draw u: u < decode_frac gives one query (a decode step), else the
+    query count is an integer drawn uniformly from [1, min(Lk, qmax)] (a
+    chunk of new tokens); Q, dO are [Tq, Hq, d] and K, V [Tk, Hkv, d], drawn
+    in the order Q, K, V, dO.
 """
 
 from __future__ import annotations
@@ -90,4 +96,34 @@ def varlen_inputs(lengths, Hq: int, Hkv: int, d: int, seed: int = 0) -> dict:
     for name, h in (("q", Hq), ("k", Hkv), ("v", Hkv), ("do", Hq)):
         out[name] = bf16_round(g.standard_normal((T, h, d), dtype=np.float32))
     out["cu_seqlens"] = cu_seqlens(lengths)
+    return out
+
+
+def qk_lengths(total_k: int = 65536, lo: int = 128, hi: int = 16384, seed: int = 2,
+               query_seed: int = 3, decode_frac: float = 0.5, qmax: int = 1024):
+    """(query lengths, key lengths) of a decode-shaped packed batch."""
+    lk = varlen_lengths(total_k, lo, hi, seed)
+    g = np.random.Generator(np.random.PCG64(query_seed))
+    lq = []
+    for k in lk:
+        u = g.uniform()
+        if u < decode_frac:
+            lq.append(1)
+        else:
+            lq.append(int(g.integers(1, min(k, qmax) + 1)))
+    return lq, lk
+
+
+def varlen_qk_inputs(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, seed: int = 0) -> dict:
+    """Packed Q, dO [Tq, Hq, d] and K, V [Tk, Hkv, d] ~ N(0, 1), bf16-rounded,
+    plus cu_seqlens_q and cu_seqlens_k."""
+    if len(lengths_q) != len(lengths_k):
+        raise ValueError("one query length and one key length per sequence")
+    tq, tk = int(np.sum(lengths_q)), int(np.sum(lengths_k))
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, t, h in (("q", tq, Hq), ("k", tk, Hkv), ("v", tk, Hkv), ("do", tq, Hq)):
+        out[name] = bf16_round(g.standard_normal((t, h, d), dtype=np.float32))
+    out["cu_seqlens_q"] = cu_seqlens(lengths_q)
+    out["cu_seqlens_k"] = cu_seqlens(lengths_k)
     return out

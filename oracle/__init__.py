@@ -15,4 +15,7 @@ from .attention import (  # noqa: F401
     head_probs,
     varlen_backward,
     varlen_forward,
+    varlen_qk_backward,
+    varlen_qk_flops,
+    varlen_qk_forward,
 )

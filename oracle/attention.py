@@ -20,6 +20,9 @@ Sources (cited by page title and section):
         column index above the row index are excluded) and 4 (MQA/GQA: K/V
         heads are shared by index mapping; the backward sums dK, dV over the
         implicitly replicated heads).
+  [FA4B] "FlashAttention-4 backward: 2-CTA mode and performance" (CSDN
+        blog), section 3.3.2: variable-length batches such as decode
+        workloads, scheduled by per-tile cost.
   The backward formulas (recompute P from the logsumexp, dV = P^T dO,
   dP = dO V^T, dS = P o (dP - D) with D = rowsum(dO o O), dK = dS^T Q,
   dQ = dS K) are the chain rule of the forward definition.  Readings taken
@@ -28,8 +31,16 @@ Sources (cited by page title and section):
       so dQ = scale * dS K and dK = scale * dS^T Q (the true gradient; pinned
       by finite differences in the tests).
     * the logsumexp is the natural log of sum_j exp(scale * q_i . k_j).
-    * causal masking is top-left aligned: key j is visible to query i iff
-      j <= i (queries and keys always have the same length here).
+    * causal masking is top-left aligned when queries and keys have the same
+      length: key j is visible to query i iff j <= i.
+    * packed batches whose sequences have different query and key lengths
+      (Lq queries against Lk keys, the decode-shaped batches of [FA4B] 3.3.2)
+      take the queries as the last Lq positions of the Lk-token context, so
+      the causal mask is bottom-right aligned: key j is visible to query i
+      iff j <= i + (Lk - Lq).
+    * a query row that sees no key at all (causal with Lq > Lk, or Lk = 0)
+      has an empty softmax: its output is 0, its logsumexp is ln 0 = -inf and
+      it contributes nothing to any gradient.
     * GQA maps query head h to key/value head h // (Hq // Hkv).
 
 Layouts (token-major, as in the library): dense Q/O/dO/dQ are [B, N, Hq, d],
@@ -55,30 +66,40 @@ def _group(hq: int, hkv: int) -> int:
     return hq // hkv
 
 
-def head_scores(qh, kh, scale: float, causal: bool, row0: int = 0) -> np.ndarray:
+def head_scores(qh, kh, scale: float, causal: bool, row0: int = 0,
+                offset: int = 0) -> np.ndarray:
     """Scaled score rows S[i, j] = scale * q_i . k_j for queries row0.. of one head.
 
-    Causal: S[i, j] = -inf where key j > query i ([FA2] "Core method" 2).
+    Causal: S[i, j] = -inf where key j > query i + offset ([FA2] "Core
+    method" 2; offset = Lk - Lq aligns the mask bottom-right, 0 when the
+    lengths are equal).
     """
     s = scale * (qh @ kh.T)
     if causal:
         rows = np.arange(row0, row0 + qh.shape[0])[:, None]
         cols = np.arange(kh.shape[0])[None, :]
-        s = np.where(cols > rows, -np.inf, s)
+        s = np.where(cols > rows + offset, -np.inf, s)
     return s
 
 
-def head_probs(qh, kh, scale: float, causal: bool, row0: int = 0):
+def head_probs(qh, kh, scale: float, causal: bool, row0: int = 0, offset: int = 0):
     """Row softmax of the scores and its natural-log normaliser.
 
     Returns (P, lse) with lse_i = ln sum_j exp(S_ij), computed stably as
     m_i + ln sum_j exp(S_ij - m_i), and P = exp(S - lse)
     ([FA2] "Problem and motivation"; "Core method" 1 for L = m + log l).
+    A row with no visible key has lse = ln 0 = -inf and P = 0.
     """
-    s = head_scores(qh, kh, scale, causal, row0)
+    s = head_scores(qh, kh, scale, causal, row0, offset)
+    if s.shape[1] == 0:
+        return s.copy(), np.full(s.shape[0], -np.inf)
     m = s.max(axis=1)
-    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-    p = np.exp(s - lse[:, None])
+    empty = m == -np.inf
+    m_safe = np.where(empty, 0.0, m)
+    with np.errstate(divide="ignore"):
+        lse = m_safe + np.log(np.exp(s - m_safe[:, None]).sum(axis=1))
+    lse = np.where(empty, -np.inf, lse)
+    p = np.where(empty[:, None], 0.0, np.exp(s - np.where(empty, 0.0, lse)[:, None]))
     return p, lse
 
 
@@ -94,18 +115,18 @@ def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
     return out
 
 
-def _head_forward(qh, kh, vh, scale, causal, row_chunk):
+def _head_forward(qh, kh, vh, scale, causal, row_chunk, offset=0):
     n = qh.shape[0]
     o = np.empty((n, vh.shape[1]))
     lse = np.empty(n)
     for r0 in range(0, n, row_chunk):
         r1 = min(n, r0 + row_chunk)
-        p, lse[r0:r1] = head_probs(qh[r0:r1], kh, scale, causal, r0)
+        p, lse[r0:r1] = head_probs(qh[r0:r1], kh, scale, causal, r0, offset)
         o[r0:r1] = p @ vh
     return o, lse
 
 
-def _head_backward(qh, kh, vh, doh, scale, causal, row_chunk):
+def _head_backward(qh, kh, vh, doh, scale, causal, row_chunk, offset=0):
     """Gradients of one query head against its key/value head.
 
     Per chunk of whole query rows: recompute P from the definition, O = P V,
@@ -119,7 +140,7 @@ def _head_backward(qh, kh, vh, doh, scale, causal, row_chunk):
     for r0 in range(0, n, row_chunk):
         r1 = min(n, r0 + row_chunk)
         q_c, do_c = qh[r0:r1], doh[r0:r1]
-        p, _ = head_probs(q_c, kh, scale, causal, r0)
+        p, _ = head_probs(q_c, kh, scale, causal, r0, offset)
         o_c = p @ vh
         d_c = (do_c * o_c).sum(axis=1)
         dv += p.T @ do_c
@@ -214,7 +235,88 @@ def varlen_backward(q, k, v, do, cu_seqlens, scale: float, causal: bool,
     return dq, dk, dv
 
 
-def head_query_rows(qh, kh, vh, doh, scale: float, causal: bool, rows):
+def _check_cu_pair(cu_q, cu_k, tq, tk):
+    cu_q, cu_k = _check_cu(cu_q, tq), _check_cu(cu_k, tk)
+    if cu_q.size != cu_k.size:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same number of sequences")
+    return cu_q, cu_k
+
+
+def varlen_qk_forward(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                      row_chunk: int = ROW_CHUNK):
+    """Packed forward with separate query and key lengths per sequence.
+
+    Sequence s has queries cu_q[s]..cu_q[s+1] and keys cu_k[s]..cu_k[s+1];
+    causal masking is bottom-right aligned (offset Lk - Lq), and rows that
+    see no key give O = 0, LSE = -inf ([FA4B] 3.3.2 decode-shaped batches).
+    q [Tq,Hq,d], k/v [Tk,Hkv,d] -> (o [Tq,Hq,d], lse [Hq,Tq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu_q, cu_k = _check_cu_pair(cu_seqlens_q, cu_seqlens_k, q.shape[0], k.shape[0])
+    Hq = q.shape[1]
+    G = _group(Hq, k.shape[1])
+    o = np.zeros_like(q)
+    lse = np.full((Hq, q.shape[0]), -np.inf)
+    for s in range(cu_q.size - 1):
+        qa, qe = int(cu_q[s]), int(cu_q[s + 1])
+        ka, ke = int(cu_k[s]), int(cu_k[s + 1])
+        if qe == qa:
+            continue
+        off = (ke - ka) - (qe - qa)
+        for h in range(Hq):
+            g = h // G
+            o[qa:qe, h], lse[h, qa:qe] = _head_forward(q[qa:qe, h], k[ka:ke, g], v[ka:ke, g],
+                                                       scale, causal, row_chunk, off)
+    return o, lse
+
+
+def varlen_qk_backward(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                       row_chunk: int = ROW_CHUNK):
+    """Packed backward with separate query and key lengths per sequence
+    -> (dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]); dK, dV summed over the
+    query heads of each group ([FA2] "Core method" 4)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    cu_q, cu_k = _check_cu_pair(cu_seqlens_q, cu_seqlens_k, q.shape[0], k.shape[0])
+    Hq = q.shape[1]
+    G = _group(Hq, k.shape[1])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for s in range(cu_q.size - 1):
+        qa, qe = int(cu_q[s]), int(cu_q[s + 1])
+        ka, ke = int(cu_k[s]), int(cu_k[s + 1])
+        if qe == qa or ke == ka:
+            continue
+        off = (ke - ka) - (qe - qa)
+        for h in range(Hq):
+            g = h // G
+            dqh, dkh, dvh = _head_backward(q[qa:qe, h], k[ka:ke, g], v[ka:ke, g], do[qa:qe, h],
+                                           scale, causal, row_chunk, off)
+            dq[qa:qe, h] = dqh
+            dk[ka:ke, g] += dkh
+            dv[ka:ke, g] += dvh
+    return dq, dk, dv
+
+
+def varlen_qk_flops(cu_seqlens_q, cu_seqlens_k, Hq: int, d: int, causal: bool):
+    """Algorithmic FLOPs of a packed batch with separate lengths: 4 d per
+    visible (query, key) pair and query head for the forward (two products),
+    2.5x that for the backward -- the dense convention counted exactly."""
+    cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
+    cu_k = np.asarray(cu_seqlens_k, dtype=np.int64)
+    pairs = 0
+    for s in range(cu_q.size - 1):
+        lq, lk = int(cu_q[s + 1] - cu_q[s]), int(cu_k[s + 1] - cu_k[s])
+        if not causal:
+            pairs += lq * lk
+            continue
+        i = np.arange(lq, dtype=np.int64)
+        pairs += int(np.clip(i + (lk - lq) + 1, 0, lk).sum())
+    f = 4.0 * Hq * d * pairs
+    return f, 2.5 * f
+
+
+def head_query_rows(qh, kh, vh, doh, scale: float, causal: bool, rows, offset: int = 0):
     """O, LSE, D and dQ of chosen query rows of one head, for spot checks at
     sizes where whole heads are too slow.
 
@@ -223,16 +325,21 @@ def head_query_rows(qh, kh, vh, doh, scale: float, causal: bool, rows):
     P_i = exp(S_i - lse_i), O_i = P_i V, D_i = dO_i . O_i, dP_i = dO_i V^T,
     dS_i = P_i o (dP_i - D_i), dQ_i = scale dS_i K  ([FA2] "Problem and
     motivation", "Core method" 1-2; the backward is the chain rule).
+    `offset` = Lk - Lq shifts the causal boundary (bottom-right alignment).
     Returns (o [r,d], lse [r], dvec [r], dq [r,d]) in the order of `rows`.
     """
     qh, kh, vh, doh = _f64(qh), _f64(kh), _f64(vh), _f64(doh)
     rows = np.asarray(rows, dtype=np.int64)
     s = scale * (qh[rows] @ kh.T)
     if causal:
-        s = np.where(np.arange(kh.shape[0])[None, :] > rows[:, None], -np.inf, s)
+        s = np.where(np.arange(kh.shape[0])[None, :] > rows[:, None] + offset, -np.inf, s)
     m = s.max(axis=1)
-    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-    p = np.exp(s - lse[:, None])
+    empty = m == -np.inf
+    m = np.where(empty, 0.0, m)
+    with np.errstate(divide="ignore"):
+        lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    p = np.where(empty[:, None], 0.0, np.exp(s - np.where(empty, 0.0, lse)[:, None]))
+    lse = np.where(empty, -np.inf, lse)
     o = p @ vh
     do_r = doh[rows]
     dvec = (do_r * o).sum(axis=1)
@@ -241,11 +348,12 @@ def head_query_rows(qh, kh, vh, doh, scale: float, causal: bool, rows):
 
 
 def head_key_rows(qh, kh, vh, doh, scale: float, causal: bool, keys,
-                  row_chunk: int = ROW_CHUNK):
+                  row_chunk: int = ROW_CHUNK, offset: int = 0):
     """dK and dV that one query head contributes to chosen keys of its
     key/value head: dV_j = sum_i P_ij dO_i and dK_j = scale sum_i dS_ij q_i.
 
-    Only queries that see a chosen key contribute (causal: i >= min(keys)),
+    Only queries that see a chosen key contribute (causal: i + offset >=
+    min(keys), offset = Lk - Lq),
     but each of them needs its whole score row for its logsumexp and for
     D_i = dO_i . O_i; rows are taken in chunks of whole rows.  Summing the
     results over the query heads of a group gives the group's dK, dV
@@ -256,11 +364,11 @@ def head_key_rows(qh, kh, vh, doh, scale: float, causal: bool, keys,
     n = qh.shape[0]
     dk = np.zeros((keys.size, kh.shape[1]))
     dv = np.zeros((keys.size, vh.shape[1]))
-    first = int(keys.min()) if causal and keys.size else 0
+    first = max(0, int(keys.min()) - offset) if causal and keys.size else 0
     for r0 in range(first, n, row_chunk):
         r1 = min(n, r0 + row_chunk)
         q_c, do_c = qh[r0:r1], doh[r0:r1]
-        p, _ = head_probs(q_c, kh, scale, causal, r0)
+        p, _ = head_probs(q_c, kh, scale, causal, r0, offset)
         d_c = (do_c * (p @ vh)).sum(axis=1)
         p_k = p[:, keys]
         ds_k = p_k * (do_c @ vh[keys].T - d_c[:, None])
