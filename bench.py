@@ -5,6 +5,11 @@ workload (B=2, H=16, N=8192, d=128, bf16, causal, fast-mode backward), with
 seeded synthetic inputs already resident in HBM.  Throughput counts the
 algorithmic FLOPs 4*B*H*N^2*d/2 (forward) + 2.5x that (backward).
 
+With --workload decode the step is instead one forward and one backward over
+a packed batch whose sequences have separate query and key lengths (decode
+steps and prefill chunks against their contexts), with FLOPs counted over the
+(query, key) pairs the bottom-right causal mask leaves visible.
+
 Prints one JSON line.  Besides the headline it carries:
   roofline      the dominant kernel (the backward main kernel): algorithmic
                 FLOPs per launch / its average duration from HIP events recorded
@@ -115,9 +120,172 @@ def cpu_baseline(B, N, Hq, Hkv, d, causal, budget_s):
     }
 
 
+DECODE_METRIC = ("attention fwd+bwd TFLOPs/s (bf16, d=128, causal, packed batch with separate "
+                 "query and key lengths) and % of MFMA peak")
+
+
+def visible_pairs(lq, lk, causal):
+    """(query, key) pairs a packed batch computes: Lq*Lk per sequence, or with
+    the bottom-right causal mask sum_i clamp(i + Lk - Lq + 1, 0, Lk)."""
+    total = 0
+    for a, b in zip(lq, lk):
+        if not causal:
+            total += a * b
+            continue
+        off = b - a
+        # rows i = 0..a-1 see min(b, max(0, i + off + 1)) keys
+        for i in range(a):
+            total += min(b, max(0, i + off + 1))
+    return total
+
+
+def decode_cpu_baseline(x, lq, lk, Hq, Hkv, d, budget_s):
+    """Oracle fwd+bwd on whole (sequence, key/value head group) slices, in
+    sequence order, until budget_s elapses; rate scaled by their FLOPs."""
+    import numpy as np
+
+    from oracle import attention as ora
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    G = Hq // Hkv
+    cq, ck = x["cu_seqlens_q"], x["cu_seqlens_k"]
+    scale = 1.0 / math.sqrt(d)
+    done_flops = 0.0
+    units = 0
+    t0 = time.perf_counter()
+    for s in range(len(lq)):
+        qa, qe, ka, ke = int(cq[s]), int(cq[s + 1]), int(ck[s]), int(ck[s + 1])
+        one_q = np.array([0, qe - qa], np.int32)
+        one_k = np.array([0, ke - ka], np.int32)
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            args = (x["q"][qa:qe, hs], x["k"][ka:ke, g:g + 1], x["v"][ka:ke, g:g + 1])
+            ora.varlen_qk_forward(*args, one_q, one_k, scale, True)
+            ora.varlen_qk_backward(*args, x["do"][qa:qe, hs], one_q, one_k, scale, True)
+            done_flops += 3.5 * 4.0 * G * d * visible_pairs([qe - qa], [ke - ka], True)
+            units += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{units} of {len(lq) * Hkv} (sequence, key/value head group) slices of the "
+                  f"same batch, fwd+bwd in fp64, {el:.1f} s; rate scaled by their algorithmic FLOPs",
+    }
+
+
+def run_decode(args):
+    """Packed batch with separate query and key lengths: 65536 keys in
+    log-uniform sequences of 128..16384 tokens, half the sequences one query
+    (a decode step), the rest a chunk of 1..1024 queries; Hq=32, Hkv=4, d=128,
+    causal (bottom-right aligned)."""
+    import numpy as np
+    import torch
+
+    from exact_attention_80_amd import fa, inputs
+
+    Hq, Hkv, d = 32, 4, 128
+    det = args.dq_mode
+    if det == 2:
+        print("bench.py: the partial-tile dQ reduction is dense-only", file=sys.stderr)
+        sys.exit(2)
+    lq, lk = inputs.qk_lengths()
+    x = inputs.varlen_qk_inputs(lq, lk, Hq, Hkv, d, seed=0)
+    t = {}
+    for n in ("q", "k", "v", "do"):
+        bits = inputs.bf16_bits(x[n]).view(np.int16)
+        t[n] = torch.from_numpy(np.ascontiguousarray(bits)).to("cuda").view(torch.bfloat16)
+    cq = torch.from_numpy(x["cu_seqlens_q"]).to("cuda")
+    ck = torch.from_numpy(x["cu_seqlens_k"]).to("cuda")
+    Tq, Tk = sum(lq), sum(lk)
+    scale = 1.0 / math.sqrt(d)
+    wsf = fa.varlen_qk_fwd_workspace(len(lq), Tq, Tk, Hq, Hkv, d, True, "cuda")
+    wsb = fa.varlen_qk_bwd_workspace(len(lq), Tq, Tk, Hq, Hkv, d, True, det, "cuda")
+
+    def step():
+        o, lse = fa.varlen_qk_fwd(t["q"], t["k"], t["v"], cq, ck, causal=True,
+                                  softmax_scale=scale, workspace=wsf)
+        fa.varlen_qk_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], cq, ck, causal=True,
+                         softmax_scale=scale, deterministic=det, workspace=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    fa.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = fa.timing_end()
+
+    pairs = visible_pairs(lq, lk, True)
+    f_fwd = 4.0 * Hq * d * pairs
+    f_bwd = 2.5 * f_fwd
+    value = (f_fwd + f_bwd) / (elapsed / args.steps) / 1e12
+    ms = {k: kt[k][1] / max(1, kt[k][0]) for k in ("fwd", "bwd_main", "bwd_pre", "bwd_post", "sched")}
+    # the dominant kernel of this workload
+    dom = "bwd_main" if ms["bwd_main"] >= ms["fwd"] else "fwd"
+    f_dom = f_bwd if dom == "bwd_main" else f_fwd
+    achieved = f_dom / (ms[dom] * 1e-3) / 1e12
+    # compulsory HBM bytes of the forward: Q, K, V read, O written (bf16), LSE (fp32)
+    fwd_bytes = 2 * d * (2 * Tq * Hq + 2 * Tk * Hkv) + 4 * Tq * Hq
+    extras = {
+        "fwd_kernel_ms": ms["fwd"], "fwd_tflops": f_fwd / (ms["fwd"] * 1e-3) / 1e12,
+        "fwd_compulsory_hbm_gbps": fwd_bytes / (ms["fwd"] * 1e-3) / 1e9,
+        "bwd_main_kernel_ms": ms["bwd_main"], "bwd_pre_ms": ms["bwd_pre"],
+        "bwd_post_ms": ms["bwd_post"], "sched_ms_per_call": ms["sched"],
+        "bwd_tflops": f_bwd / (ms["bwd_main"] * 1e-3) / 1e12,
+        "visible_pairs_per_head": pairs, "nseq": len(lq), "total_q": Tq, "total_k": Tk,
+    }
+    line = {
+        "metric": DECODE_METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"causal packed batch with separate query and key lengths: {len(lq)} "
+                        f"sequences, {Tq} queries against {Tk} keys (half one-query decode steps), "
+                        f"Hq={Hq} Hkv={Hkv} d={d}, "
+                        f"{('atomic', 'semaphore-ordered')[det]} dQ reduction",
+            "nseq": len(lq), "total_q": Tq, "total_k": Tk, "Hq": Hq, "Hkv": Hkv, "d": d,
+            "causal": True, "deterministic": det,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": {"bwd_main": "bwd_kernel (backward main)", "fwd": "fwd_kernel"}[dom],
+            "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+        },
+        "extras": extras,
+    }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = decode_cpu_baseline(x, lq, lk, Hq, Hkv, d, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="headline", choices=("headline", "decode"),
+                    help="headline: causal B=2 H=16 N=8192 d=128; decode: packed batch with "
+                         "separate query and key lengths (Hq=32, Hkv=4, d=128)")
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--B", type=int, default=2)
@@ -153,6 +321,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n}), flush=True)
+        return
+
+    if args.workload == "decode":
+        torch.cuda.set_device(0)
+        run_decode(args)
         return
 
     from exact_attention_80_amd import fa

@@ -193,14 +193,15 @@ int choose_split(long units, int G) {
   return G;
 }
 
-BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, int Hq, int Hkv, int d,
+// T: query tokens, Tk: key tokens (equal for dense calls)
+BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, long Tk, int Hq, int Hkv, int d,
                      int deterministic, bool causal) {
   BwdLayout l;
   const int G = Hq / Hkv;
   long units;
   if (varlen) {
-    l.max_tiles = (int)(T / fa::kBwdBC + nseq);
-    units = (long)Hkv * (T / fa::kBwdBC + 1);
+    l.max_tiles = (int)(Tk / fa::kBwdBC + nseq);
+    units = (long)Hkv * (Tk / fa::kBwdBC + 1);
   } else {
     units = (long)B * Hkv * cdiv(N, fa::kBwdBC);
   }
@@ -234,9 +235,9 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, int Hq, int Hk
   }
   if (l.S > 1) {
     l.dk_part = off;
-    off += align_up((size_t)l.S * T * Hkv * d * 4);
+    off += align_up((size_t)l.S * Tk * Hkv * d * 4);
     l.dv_part = off;
-    off += align_up((size_t)l.S * T * Hkv * d * 4);
+    off += align_up((size_t)l.S * Tk * Hkv * d * 4);
   }
   l.total = off;
   return l;
@@ -251,15 +252,19 @@ int hip_fail(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 // shared implementations of dense and varlen calls
 
+// cu / T: query offsets and tokens; cu_k / Tk: key offsets and tokens
+// (cu_k == cu and Tk == T for calls with equal lengths)
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, int B,
-            int N, const int32_t* cu, int nseq, long T, int Hq, int Hkv, int d, float scale,
-            int causal, void* ws, size_t ws_bytes, void* stream) {
+            int N, const int32_t* cu, const int32_t* cu_k, int nseq, long T, long Tk, int Hq,
+            int Hkv, int d, float scale, int causal, void* ws, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
     return st;
-  if (varlen && (st = check_ptr(cu, "cu_seqlens"))) return st;
+  if (varlen && ((st = check_ptr(cu, "cu_seqlens_q")) || (st = check_ptr(cu_k, "cu_seqlens_k"))))
+    return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
+  if ((st = check_dims(Tk, Hq, Hkv, d, causal, scale))) return st;
   const FwdLayout lay = fwd_layout(varlen, nseq, T);
   if (ws_bytes < lay.total || (lay.total > 0 && !ws))
     return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*fwd_workspace_size()");
@@ -289,11 +294,12 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
     uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, lay.hdr));
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
     const long tk = timing_start(4, s);
-    e = fa::launch_sched(cu, nseq, (int)T, br, 0, causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ,
-                         tiles, lay.max_tiles, hdr, s);
+    e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, br, 0, causal != 0, fa::fwd_tile_keys(),
+                         fa::kBwdBQ, tiles, lay.max_tiles, hdr, s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
+    p.cu_seqlens_k = cu_k;
     p.tiles = tiles;
     p.hdr = hdr;
     grid = (long)lay.max_tiles * Hq;
@@ -312,20 +318,24 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
 
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, void* dq, void* dk, void* dv, bool varlen, int B, int N,
-            const int32_t* cu, int nseq, long T, int Hq, int Hkv, int d, float scale, int causal,
-            int deterministic, void* ws, size_t ws_bytes, void* stream) {
+            const int32_t* cu, const int32_t* cu_k, int nseq, long T, long Tk, int Hq, int Hkv,
+            int d, float scale, int causal, int deterministic, void* ws, size_t ws_bytes,
+            void* stream) {
   int st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(lse, "lse")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
     return st;
-  if (varlen && (st = check_ptr(cu, "cu_seqlens"))) return st;
+  if (varlen && ((st = check_ptr(cu, "cu_seqlens_q")) || (st = check_ptr(cu_k, "cu_seqlens_k"))))
+    return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
+  if ((st = check_dims(Tk, Hq, Hkv, d, causal, scale))) return st;
   if (deterministic < 0 || deterministic > 2)
     return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1 or 2");
   if (varlen && deterministic == 2)
     return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 (partial-sum dQ) is dense-only");
-  const BwdLayout lay = bwd_layout(varlen, B, N, nseq, T, Hq, Hkv, d, deterministic, causal != 0);
+  const BwdLayout lay =
+      bwd_layout(varlen, B, N, nseq, T, Tk, Hq, Hkv, d, deterministic, causal != 0);
   if (!ws || ws_bytes < lay.total)
     return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*bwd_workspace_size()");
   if ((st = check_ptr(ws, "ws"))) return st;
@@ -369,6 +379,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   p.G = Hq / Hkv;
   p.S = lay.S;
   p.T = (int)T;
+  p.Tk = (int)Tk;
   p.sem_slots = lay.sem_slots;
   p.sched = sched_mode();
   p.c = scale * fa::kLog2e;
@@ -378,11 +389,13 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (varlen) {
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
     tk = timing_start(4, s);
-    e = fa::launch_sched(cu, nseq, (int)T, fa::kBwdBC, deterministic ? 2 : 1, causal != 0,
-                         fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles, hdr, s);
+    e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, fa::kBwdBC, deterministic ? 2 : 1,
+                         causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles, hdr,
+                         s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
+    p.cu_seqlens_k = cu_k;
     p.tiles = tiles;
     grid = (long)lay.max_tiles * Hkv * lay.S;
   } else {
@@ -404,11 +417,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     if (e == hipSuccess && lay.S > 1)
       e = fa::launch_bwd_post(nullptr, nullptr, 0, scale, p.dk_part, p.dv_part,
                               static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
-                              T * Hkv * d, lay.S, s);
+                              Tk * Hkv * d, lay.S, s);
   } else {
     e = fa::launch_bwd_post(dq_acc, static_cast<fa::bf16*>(dq), T * Hq * d, scale, p.dk_part,
                             p.dv_part, static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
-                            T * Hkv * d, lay.S, s);
+                            Tk * Hkv * d, lay.S, s);
   }
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward post launch");
@@ -447,15 +460,16 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
            void* stream) {
   if (!dense_ok(B, N)) return fail(FA_ERR_INVALID_ARG, "B and N must be positive");
-  return run_fwd(q, k, v, o, lse, false, B, N, nullptr, 0, (long)B * N, Hq, Hkv, d,
-                 softmax_scale, causal, ws, ws_bytes, stream);
+  return run_fwd(q, k, v, o, lse, false, B, N, nullptr, nullptr, 0, (long)B * N, (long)B * N, Hq,
+                 Hkv, d, softmax_scale, causal, ws, ws_bytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
   if (deterministic < 0 || deterministic > 2) return 0;
-  return bwd_layout(false, B, N, 0, (long)B * N, Hq, Hkv, d, deterministic, causal != 0).total;
+  return bwd_layout(false, B, N, 0, (long)B * N, (long)B * N, Hq, Hkv, d, deterministic,
+                    causal != 0).total;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -463,8 +477,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            float softmax_scale, int causal, int deterministic, void* ws, size_t ws_bytes,
            void* stream) {
   if (!dense_ok(B, N)) return fail(FA_ERR_INVALID_ARG, "B and N must be positive");
-  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, false, B, N, nullptr, 0, (long)B * N, Hq, Hkv,
-                 d, softmax_scale, causal, deterministic, ws, ws_bytes, stream);
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, false, B, N, nullptr, nullptr, 0, (long)B * N,
+                 (long)B * N, Hq, Hkv, d, softmax_scale, causal, deterministic, ws, ws_bytes,
+                 stream);
 }
 
 size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
@@ -480,8 +495,8 @@ int fa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   void* stream) {
   if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
   if (max_seqlen < 0) return fail(FA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
-  return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens, nseq, total_tokens, Hq, Hkv, d,
-                 softmax_scale, causal, ws, ws_bytes, stream);
+  return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens, cu_seqlens, nseq, total_tokens,
+                 total_tokens, Hq, Hkv, d, softmax_scale, causal, ws, ws_bytes, stream);
 }
 
 size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
@@ -489,7 +504,8 @@ size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv,
   (void)causal;
   if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
   if (deterministic < 0 || deterministic > 1) return 0;
-  return bwd_layout(true, 0, 0, nseq, total_tokens, Hq, Hkv, d, deterministic, causal != 0).total;
+  return bwd_layout(true, 0, 0, nseq, total_tokens, total_tokens, Hq, Hkv, d, deterministic,
+                    causal != 0).total;
 }
 
 int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -499,8 +515,50 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, co
                   void* stream) {
   if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
   if (max_seqlen < 0) return fail(FA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
-  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, true, 1, 0, cu_seqlens, nseq, total_tokens,
-                 Hq, Hkv, d, softmax_scale, causal, deterministic, ws, ws_bytes, stream);
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, true, 1, 0, cu_seqlens, cu_seqlens, nseq,
+                 total_tokens, total_tokens, Hq, Hkv, d, softmax_scale, causal, deterministic, ws,
+                 ws_bytes, stream);
+}
+
+size_t fa_varlen_qk_fwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
+                                       int d, int causal) {
+  (void)total_k; (void)Hq; (void)Hkv; (void)d; (void)causal;
+  if (nseq <= 0 || total_q <= 0) return 0;
+  return fwd_layout(true, nseq, total_q).total;
+}
+
+int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                     int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                     int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
+  if (max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q and max_seqlen_k must be >= 0");
+  return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
+                 Hq, Hkv, d, softmax_scale, causal, ws, ws_bytes, stream);
+}
+
+size_t fa_varlen_qk_bwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
+                                       int d, int causal, int deterministic) {
+  if (nseq <= 0 || total_q <= 0 || total_k <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+  if (deterministic < 0 || deterministic > 1) return 0;
+  return bwd_layout(true, 0, 0, nseq, total_q, total_k, Hq, Hkv, d, deterministic, causal != 0)
+      .total;
+}
+
+int fa_varlen_qk_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                     int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                     int Hkv, int d, float softmax_scale, int causal, int deterministic, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
+  if (max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q and max_seqlen_k must be >= 0");
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq,
+                 total_q, total_k, Hq, Hkv, d, softmax_scale, causal, deterministic, ws, ws_bytes,
+                 stream);
 }
 
 int fa_timing_begin(void) {

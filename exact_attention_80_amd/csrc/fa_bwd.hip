@@ -22,6 +22,11 @@
 //    the causal walk (diagonal first) never stalls on its first write.
 //  * post: dQ = bf16(scale * dQ_acc); split subgroups' dK/dV partials are
 //    summed in a fixed order.
+// A packed sequence may have Lq queries and Lk keys (the decode-shaped
+// batches of [FA4B] 3.3.2): the causal diagonal is then aligned bottom-right
+// (query i sees key j iff j <= i + Lk - Lq), the walk of a key tile starts at
+// the first query tile that sees it, and rows that see no key carry
+// LSE = -inf, which the preprocess turns into P = 0.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -113,10 +118,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     it.jt = p.tiles[2 * e + 1];
     it.hkv = u / p.S;
     it.split = u - it.hkv * p.S;
-    it.seq_start = p.cu_seqlens[it.seq];
-    it.seq_len = p.cu_seqlens[it.seq + 1] - it.seq_start;
-    it.nq = (it.seq_len + BQ - 1) / BQ;
-    it.nkv = (it.seq_len + BC - 1) / BC;
+    it.q_start = p.cu_seqlens[it.seq];
+    it.q_len = p.cu_seqlens[it.seq + 1] - it.q_start;
+    it.k_start = p.cu_seqlens_k[it.seq];
+    it.k_len = p.cu_seqlens_k[it.seq + 1] - it.k_start;
+    it.off = it.k_len - it.q_len;
+    it.nq = (it.q_len + BQ - 1) / BQ;
+    it.nkv = (it.k_len + BC - 1) / BC;
   } else {
     const int U = p.B * HS;
     int u, jj;
@@ -140,8 +148,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     it.hkv = rest / p.S;
     it.split = rest - it.hkv * p.S;
     it.jt = jj;
-    it.seq_start = it.seq * p.N;
-    it.seq_len = p.N;
+    it.q_start = it.seq * p.N;
+    it.q_len = p.N;
+    it.k_start = it.q_start;
+    it.k_len = p.N;
+    it.off = 0;
     it.nq = p.nq;
     it.nkv = p.nkv;
   }
@@ -153,13 +164,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int key0 = it.jt * BC;
   const int wk0 = key0 + wave * 32;  // this wave's first key
   const int mykey = wk0 + l32;
-  const bool key_ok = mykey < it.seq_len;
-  const int last = it.seq_len - 1;
+  const bool key_ok = mykey < it.k_len;
+  const int klast = it.k_len - 1;  // last key row (row clamp of the K copy)
+  const int qlast = it.q_len - 1;  // last query row
 
   // ---------------- K tile -> LDS (direct), V rows of this wave -> registers
-  const bf16* kseq = p.k + (long)it.seq_start * kv_row + (long)it.hkv * D;
-  const bf16* vseq = p.v + (long)it.seq_start * kv_row + (long)it.hkv * D;
-  dma_swz_tile<KT, ST, NW>(k_s, kseq, kv_row, key0, last, wave, lane);
+  const bf16* kseq = p.k + (long)it.k_start * kv_row + (long)it.hkv * D;
+  const bf16* vseq = p.v + (long)it.k_start * kv_row + (long)it.hkv * D;
+  dma_swz_tile<KT, ST, NW>(k_s, kseq, kv_row, key0, klast, wave, lane);
   bf16x8 vf[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
@@ -175,8 +187,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) { dk_acc[db][x] = 0.f; dv_acc[db][x] = 0.f; }
 
-  // ---------------- walk over (head, query tile)
-  const int i_start = CAUSAL ? (key0 / BQ) : 0;
+  // ---------------- walk over (head, query tile); causal: from the first
+  // query tile holding a query that sees key0 (query >= key0 - off)
+  const int i_start = CAUSAL ? max(0, key0 - it.off) / BQ : 0;
   const int nsteps = max(0, it.nq - i_start);
   const int nitems = GS * nsteps;
 
@@ -189,17 +202,17 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const int i = i_start + (item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
-    const long tok = (long)it.seq_start + q0;
-    const uint32_t range = tile_range(q0, it.seq_len, q_row * 2, D * 2);
+    const long tok = (long)it.q_start + q0;
+    const uint32_t range = tile_range(q0, it.q_len, q_row * 2, D * 2);
     qcopy.issue(qd, make_rsrc(p.q + tok * q_row + (long)h * D, range));
     qcopy.issue(dod, make_rsrc(p.dout + tok * q_row + (long)h * D, range));
     if (wave == NW - 1) {
       // lanes 0..31 copy the tile's LSE values, lanes 32..63 its D values;
       // both land at std_ + 4*lane, so the buffer holds LSE[BQ] then D[BQ]
       long base;
-      if (VARLEN) base = (long)h * p.T + it.seq_start;
+      if (VARLEN) base = (long)h * p.T + it.q_start;
       else base = ((long)it.seq * p.Hq + h) * p.N;
-      const int q = min(q0 + l32, last);
+      const int q = min(q0 + l32, qlast);
       if (half == 0) dma4(p.lse + base + q, std_);
       else dma4(p.dvec + base + q, std_);
     }
@@ -278,25 +291,36 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int qb = 0; qb < NQB; ++qb) *reinterpret_cast<f32x4*>(dst + qb * 256) = acc[qb];
       return;
     }
-    float* dq_base = p.dq_acc + (long)it.seq_start * q_row + (long)h * D + dblk * 16 + L16;
     if (!DET) {
-      // exactly 4 NQB atomic instructions per wave (rows past the end add 0
-      // to the last row), so the next item can wait for its copies alone
+      // exactly 4 NQB atomic instructions per wave, so the next item can wait
+      // for its copies alone: they go through a buffer descriptor whose range
+      // ends at the tile's last valid row, and the hardware drops the ones
+      // for rows past the sequence end (no traffic, and no pile-up of many
+      // workgroups' adds on one clamped address when a sequence has a single
+      // query)
+      const int nvalid = min(BQ, it.q_len - q0);
+      const float* tile0 = p.dq_acc + ((long)it.q_start + q0) * q_row + (long)h * D;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(tile0), (short)0, (int)(((nvalid - 1) * q_row + D) * 4), 0x00020000);
+      // byte offset of this lane's element in row 16 qb0 + 4 g16 of the tile;
+      // rebuilt per item (the empty asm keeps the compiler from holding 4 NQB
+      // offsets in registers across the whole loop)
+      int vo = ((16 * qb0 + 4 * g16) * (int)q_row + dblk * 16 + L16) * 4;
+      asm volatile("" : "+v"(vo));
+      const int row_bytes = (int)q_row * 4;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
-          __hip_atomic_fetch_add(dq_base + (long)min(q, last) * q_row,
-                                 q < it.seq_len ? acc[qb][r] : 0.f, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int r = 0; r < 4; ++r)
+          (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+              acc[qb][r], rsrc, vo + (16 * qb + r) * row_bytes, 0, 0);
     } else {
+      float* dq_base = p.dq_acc + (long)it.q_start * q_row + (long)h * D + dblk * 16 + L16;
       // ordered reduction: writers of a dQ tile apply in descending key-tile order
-      const int jhi = CAUSAL ? min(it.nkv - 1, (q0 + BQ - 1) / BC) : it.nkv - 1;
+      const int jhi = CAUSAL ? min(it.nkv - 1, (q0 + BQ - 1 + it.off) / BC) : it.nkv - 1;
       const int rank = jhi - it.jt;
       long sidx;
-      if (VARLEN) sidx = (long)h * p.sem_slots + it.seq_start / BQ + it.seq + i;
+      if (VARLEN) sidx = (long)h * p.sem_slots + it.q_start / BQ + it.seq + i;
       else sidx = ((long)it.seq * p.Hq + h) * p.nq + i;
       int* semp = p.sem + sidx;
       // Wait for our turn.  The semaphore and the dQ accumulator are only ever
@@ -326,7 +350,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
-          if (q < it.seq_len)
+          if (q < it.q_len)
             __hip_atomic_fetch_add(dq_base + (long)q * q_row, acc[qb][r], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -344,7 +368,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const int h = h0 + hh;
     const int q0 = i * BQ;
 
-    const bool active = wk0 < it.seq_len && (!CAUSAL || q0 + BQ - 1 >= wk0);
+    const int koff = VARLEN ? it.off : 0;  // causal diagonal offset Lk - Lq
+    const bool active = wk0 < it.k_len && (!CAUSAL || q0 + BQ - 1 + koff >= wk0);
     if (active) {
       f32x16 s, dp;
 #pragma unroll
@@ -362,8 +387,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       // s[x] = S[q = q0 + 8(x/4) + 4 half + x%4][key = mykey]
       const float* lse_s = reinterpret_cast<const float*>(sts);
       const float* dv_s = lse_s + BQ;
-      const bool need_mask = (CAUSAL && q0 < wk0 + 31) || (wk0 + 32 > it.seq_len) ||
-                             (q0 + BQ > it.seq_len);
+      const bool need_mask = (CAUSAL && q0 + koff < wk0 + 31) || (wk0 + 32 > it.k_len) ||
+                             (q0 + BQ > it.q_len);
       // P = exp2(S c - LSE log2 e), dS = P o (dP - D); with a causal mask the
       // masked copy runs on diagonal and ragged tiles only (a uniform branch)
       auto softmax_grad = [&](auto masked) {
@@ -377,7 +402,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             float pr = fast_exp2(fmaf(s[x], p.c, -l4[e]));
             if (decltype(masked)::value) {
               const int q = q0 + 8 * g + 4 * half + e;
-              if (!key_ok || q >= it.seq_len || (CAUSAL && mykey > q)) pr = 0.f;
+              if (!key_ok || q >= it.q_len || (CAUSAL && mykey > q + koff)) pr = 0.f;
             }
             s[x] = pr;
             dp[x] = pr * (dp[x] - d4[e]);
@@ -464,13 +489,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int key = wk0 + 8 * (x >> 2) + 4 * half + (x & 3);
-      if (key < it.seq_len) {
-        const long off = ((long)it.seq_start + key) * kv_row + (long)it.hkv * D + db * 32 + l32;
+      if (key < it.k_len) {
+        const long off = ((long)it.k_start + key) * kv_row + (long)it.hkv * D + db * 32 + l32;
         if (p.S == 1) {
           p.dk[off] = (bf16)(dk_acc[db][x] * p.scale);
           p.dv[off] = (bf16)(dv_acc[db][x]);
         } else {
-          const long po = (long)it.split * p.T * kv_row + off;
+          const long po = (long)it.split * p.Tk * kv_row + off;
           p.dk_part[po] = dk_acc[db][x] * p.scale;
           p.dv_part[po] = dv_acc[db][x];
         }
@@ -546,7 +571,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
       idx = ((long)b * Hq + h) * N + n;
     }
     dvec[idx] = acc;
-    lse2[idx] = lse[idx] * kLog2e;
+    // a row that saw no key (LSE = -inf) gets +inf, so P = exp2(S c - LSE2) = 0
+    const float l = lse[idx];
+    lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 

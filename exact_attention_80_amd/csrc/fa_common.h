@@ -383,11 +383,12 @@ struct FwdParams {
   const bf16* v;
   bf16* o;
   float* lse;
-  const int* cu_seqlens;  // varlen only
+  const int* cu_seqlens;  // varlen only: query offsets
+  const int* cu_seqlens_k;  // varlen only: key offsets (the same array when Lq == Lk)
   const int* tiles;       // varlen only: (sequence, q-tile) pairs in schedule order
   const uint32_t* hdr;    // varlen only: workspace header (error word, tile count)
   int B, N, Hq, Hkv, G;   // dense: N is the sequence length
-  int T;                  // total tokens (varlen LSE layout [Hq, T])
+  int T;                  // total query tokens (varlen LSE layout [Hq, T])
   int nq;                 // dense: number of query tiles per sequence
   int sched;              // 0: longest-first, XCD-grouped; 1: natural order
   float c;                // softmax_scale * log2(e)
@@ -397,8 +398,11 @@ struct FwdParams {
 // query-head subgroup).
 struct BwdItem {
   int seq;        // batch index (dense) or sequence index (varlen)
-  int seq_start;
-  int seq_len;
+  int q_start;    // first query token, and the sequence's query count
+  int q_len;
+  int k_start;    // first key token, and the sequence's key count
+  int k_len;
+  int off;        // causal offset k_len - q_len: key j is visible to query i iff j <= i + off
   int hkv;
   int split;      // query-head subgroup
   int jt;         // key tile
@@ -416,16 +420,18 @@ struct BwdParams {
   float* dq_acc;          // [T, Hq, d] fp32
   bf16* dk;
   bf16* dv;
-  float* dk_part;         // [S, T, Hkv, d] fp32 when S > 1
+  float* dk_part;         // [S, Tk, Hkv, d] fp32 when S > 1
   float* dv_part;
   int* sem;               // dQ tile semaphores (ordered mode)
   float* dq_part;         // per-(query tile, key tile) dQ partial tiles (partial-sum mode)
   long head_pairs;        // partial tiles per (sequence, query head)
   uint32_t* hdr;          // workspace header
-  const int* cu_seqlens;  // varlen only
+  const int* cu_seqlens;  // varlen only: query offsets
+  const int* cu_seqlens_k;  // varlen only: key offsets (the same array when Lq == Lk)
   const int* tiles;       // varlen only: (sequence, kv-tile) pairs in schedule order
   int B, N, Hq, Hkv, G, S;
-  int T;
+  int T;                  // total query tokens
+  int Tk;                 // total key tokens
   int nkv;                // dense: number of key tiles per sequence
   int nq;                 // dense: number of query tiles per sequence
   int sem_slots;          // varlen: semaphore slots per head

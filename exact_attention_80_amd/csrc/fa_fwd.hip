@@ -20,7 +20,11 @@
 //    order the P fragment already has) and is divided by the row sum once at
 //    the end; only LSE = ln(sum exp) is saved;
 //  * causal: key tiles wholly above a wave's rows are skipped, the mask is
-//    applied only on tiles that straddle the diagonal or the sequence end.
+//    applied only on tiles that straddle the diagonal or the sequence end;
+//    a packed sequence with Lq queries and Lk keys aligns the diagonal
+//    bottom-right (query i sees key j iff j <= i + Lk - Lq, the decode-shaped
+//    batches of [FA4B] 3.3.2), and a query that sees no key gets O = 0 and
+//    LSE = -inf.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -32,8 +36,11 @@ constexpr int kBC = 64;        // keys per K/V tile
 constexpr float kTau = 8.0f;   // rescale threshold (log2 units): p <= 2^8
 
 struct WorkItem {
-  int seq_start;  // first token of the sequence
-  int seq_len;
+  int seq_start;  // first query token of the sequence
+  int seq_len;    // its query count
+  int k_start;    // first key token
+  int k_len;      // key count
+  int off;        // causal offset k_len - seq_len
   int b;          // batch index (dense) or sequence index (varlen)
   int h;          // query head
   int qtile;
@@ -54,6 +61,9 @@ __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
     w.qtile = p.tiles[2 * e + 1];
     w.seq_start = p.cu_seqlens[w.b];
     w.seq_len = p.cu_seqlens[w.b + 1] - w.seq_start;
+    w.k_start = p.cu_seqlens_k[w.b];
+    w.k_len = p.cu_seqlens_k[w.b + 1] - w.k_start;
+    w.off = w.k_len - w.seq_len;
   } else {
     const int BH = p.B * p.Hq;
     int i, bh;
@@ -78,6 +88,9 @@ __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
     w.qtile = i;
     w.seq_start = w.b * p.N;
     w.seq_len = p.N;
+    w.k_start = w.seq_start;
+    w.k_len = p.N;
+    w.off = 0;
     w.valid = true;
   }
   return w;
@@ -110,8 +123,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const long q_row = (long)p.Hq * D;   // elements between consecutive tokens
   const long kv_row = (long)p.Hkv * D;
   const bf16* qbase = p.q + (long)wi.seq_start * q_row + (long)wi.h * D;
-  const bf16* kbase = p.k + (long)wi.seq_start * kv_row + (long)hkv * D;
-  const bf16* vbase = p.v + (long)wi.seq_start * kv_row + (long)hkv * D;
+  const bf16* kbase = p.k + (long)wi.k_start * kv_row + (long)hkv * D;
+  const bf16* vbase = p.v + (long)wi.k_start * kv_row + (long)hkv * D;
+  const int klen = wi.k_len;
+  const int off = wi.off;
 
   // ---- this lane's query and its Q fragments (operand B of S^T = K Q^T)
   const int wq0 = q0 + wave * 32;
@@ -125,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     qf[dc] = as_bf16x8(u);
   }
 
-  const int kv_end = CAUSAL ? min(wi.seq_len, q0 + BR) : wi.seq_len;
+  const int kv_end = CAUSAL ? max(0, min(klen, q0 + BR + off)) : klen;
   const int nt = (kv_end + kBC - 1) / kBC;
 
   // ---- direct global->LDS copy of one K and one V tile.  Rows past the
@@ -140,7 +155,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   vcopy.init(kv_bytes, VST, wave, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
   auto issue_tile = [&](int j) {
     char* kt = kv_s[j % STAGES];
-    const uint32_t range = tile_range(j * kBC, wi.seq_len, kv_bytes, D * 2);
+    const uint32_t range = tile_range(j * kBC, klen, kv_bytes, D * 2);
     kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * kv_row, range));
     vcopy.issue(kt + KT::kBytes, make_rsrc(vbase + (long)j * kBC * kv_row, range));
   };
@@ -175,14 +190,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
         s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
       }
     }
-    const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0) || (key0 + kBC > wi.seq_len);
+    const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0 + off) || (key0 + kBC > klen);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool dead = key >= wi.seq_len || (CAUSAL && key > qi);
+          const bool dead = key >= klen || (CAUSAL && key > qi + off);
           if (dead) s[kb][r] = -INFINITY;
         }
     }
@@ -247,10 +262,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     compute_tile(j, kt, kt + KT::kBytes);
   }
 
-  // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2;
+  // a row that saw no key (l = 0) stores O = 0 and LSE = -inf
   const float ltot = halves_sum(lsum);
   if (!q_ok) return;
-  const float inv = 1.0f / ltot;
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
   bf16* orow = p.o + ((long)wi.seq_start + qi) * q_row + (long)wi.h * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       *reinterpret_cast<u32x2*>(orow + d0) = w;
     }
   if (half == 0) {
-    const float lse = (m_ref + log2f(ltot)) * kLn2;
+    const float lse = ltot > 0.f ? (m_ref + log2f(ltot)) * kLn2 : -INFINITY;
     long idx;
     if (VARLEN) idx = (long)wi.h * p.T + wi.seq_start + qi;
     else idx = ((long)wi.b * p.Hq + wi.h) * p.N + qi;

@@ -57,16 +57,18 @@ hipError_t launch_bwd_dq_reduce(const float* part, bf16* dq, int B, int N, int H
 long bwd_partial_pairs(int N, bool causal);
 
 // dQ = bf16(scale * dQ_acc); when S > 1 also dK/dV = bf16(sum of the S partials).
+// dq_elems counts query-side elements, kv_elems key-side ones.
 hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float scale,
                            const float* dk_part, const float* dv_part, bf16* dk, bf16* dv,
                            long kv_elems, int S, hipStream_t stream);
 
-// Variable-length scheduler: validates cu_seqlens and writes the ordered work list.
+// Variable-length scheduler: validates the query and key offsets (cu_q and
+// cu_k may be the same array) and writes the ordered work list.
 //   mode 0: forward query tiles, longest first
 //   mode 1: backward key tiles, longest first
 //   mode 2: backward key tiles, deterministic order (key tiles of a sequence last-first)
-hipError_t launch_sched(const int* cu_seqlens, int nseq, int total, int tile, int mode,
-                        bool causal, int fwd_kv_tile, int bwd_q_tile, int* tiles, int max_tiles,
-                        uint32_t* hdr, hipStream_t stream);
+hipError_t launch_sched(const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k,
+                        int tile, int mode, bool causal, int fwd_kv_tile, int bwd_q_tile,
+                        int* tiles, int max_tiles, uint32_t* hdr, hipStream_t stream);
 
 }  // namespace fa

@@ -12,7 +12,11 @@
 //           key tile is always issued after every key tile it waits for.
 // The ordering only changes which work runs when, never any result.  Lists
 // longer than the in-LDS sort capacity are written in natural order (still
-// last-tile-first within a sequence for mode 2).
+// last-tile-first within a sequence for mode 2).  Query and key offsets are
+// separate arrays (the same one when every sequence has Lq == Lk); forward
+// tiles split a sequence's queries, backward tiles its keys, and the cost of
+// a tile counts the inner tiles its causal walk visits with the diagonal
+// aligned bottom-right (offset Lk - Lq).
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -26,14 +30,22 @@ constexpr int kSortCap = 8192;  // 64 KiB of 64-bit keys
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // cost of one tile in units of the inner loop's tiles
-__device__ __forceinline__ int tile_cost(int mode, bool causal, int len, int tile, int idx,
+__device__ __forceinline__ int tile_cost(int mode, bool causal, int lq, int lk, int tile, int idx,
                                         int fkv, int bq) {
+  const int off = lk - lq;
   if (mode == 0) {
-    const int end = causal ? min(len, (idx + 1) * tile) : len;
+    const int end = causal ? max(0, min(lk, (idx + 1) * tile + off)) : lk;
     return cdiv(end, fkv);
   }
-  const int nq = cdiv(len, bq);
-  return causal ? nq - (idx * tile) / bq : nq;
+  const int nq = cdiv(lq, bq);
+  return causal ? max(0, nq - max(0, idx * tile - off) / bq) : nq;
+}
+
+// tiles of sequence s: its query rows (forward) or its keys (backward)
+__device__ __forceinline__ int seq_tiles(int mode, const int* cu_q, const int* cu_k, int s,
+                                         int tile) {
+  const int* cu = mode == 0 ? cu_q : cu_k;
+  return cdiv(cu[s + 1] - cu[s], tile);
 }
 
 __device__ __forceinline__ unsigned long long sort_key(int mode, int cost, int seq, int idx) {
@@ -54,7 +66,8 @@ __device__ __forceinline__ void decode_key(int mode, unsigned long long k, int& 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu, int nseq, int total,
+__global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const int* cu_k,
+                                                         int nseq, int total_q, int total_k,
                                                          int tile, int mode, int causal, int fkv,
                                                          int bq, int* tiles, int max_tiles,
                                                          uint32_t* hdr) {
@@ -68,10 +81,13 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu, int nseq
   }
   __syncthreads();
 
-  // ---- validation: cu[0] == 0, cu[nseq] == total, non-decreasing
+  // ---- validation of both offset arrays: cu[0] == 0, cu[nseq] == total,
+  // non-decreasing
   for (int s = tid; s < nseq; s += kThreads) {
-    const int a = cu[s], b = cu[s + 1];
-    if (b < a || (s == 0 && a != 0) || (s == nseq - 1 && b != total)) atomicOr(&bad, 1);
+    const int a = cu_q[s], b = cu_q[s + 1];
+    if (b < a || (s == 0 && a != 0) || (s == nseq - 1 && b != total_q)) atomicOr(&bad, 1);
+    const int c = cu_k[s], e = cu_k[s + 1];
+    if (e < c || (s == 0 && c != 0) || (s == nseq - 1 && e != total_k)) atomicOr(&bad, 1);
   }
   __syncthreads();
   if (bad) {
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu, int nseq
   const int per = cdiv(nseq, kThreads);
   const int s_lo = min(nseq, tid * per), s_hi = min(nseq, s_lo + per);
   int mine = 0;
-  for (int s = s_lo; s < s_hi; ++s) mine += cdiv(cu[s + 1] - cu[s], tile);
+  for (int s = s_lo; s < s_hi; ++s) mine += seq_tiles(mode, cu_q, cu_k, s, tile);
   scan[tid] = mine;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
@@ -109,10 +125,10 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu, int nseq
     int n = 1;
     while (n < count) n <<= 1;
     for (int s = s_lo; s < s_hi; ++s) {
-      const int len = cu[s + 1] - cu[s];
-      const int nt = cdiv(len, tile);
+      const int lq = cu_q[s + 1] - cu_q[s], lk = cu_k[s + 1] - cu_k[s];
+      const int nt = seq_tiles(mode, cu_q, cu_k, s, tile);
       for (int i = 0; i < nt; ++i)
-        keys[pos++] = sort_key(mode, tile_cost(mode, causal != 0, len, tile, i, fkv, bq), s, i);
+        keys[pos++] = sort_key(mode, tile_cost(mode, causal != 0, lq, lk, tile, i, fkv, bq), s, i);
     }
     for (int x = count + tid; x < n; x += kThreads) keys[x] = ~0ull;
     __syncthreads();
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu, int nseq
     }
   } else {
     for (int s = s_lo; s < s_hi; ++s) {
-      const int nt = cdiv(cu[s + 1] - cu[s], tile);
+      const int nt = seq_tiles(mode, cu_q, cu_k, s, tile);
       for (int i = 0; i < nt; ++i) {
         tiles[2 * pos] = s;
         tiles[2 * pos + 1] = mode == 2 ? nt - 1 - i : i;
@@ -154,11 +170,12 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu, int nseq
 
 }  // namespace
 
-hipError_t launch_sched(const int* cu_seqlens, int nseq, int total, int tile, int mode,
-                        bool causal, int fwd_kv_tile, int bwd_q_tile, int* tiles, int max_tiles,
-                        uint32_t* hdr, hipStream_t stream) {
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, cu_seqlens, nseq, total,
-                     tile, mode, causal ? 1 : 0, fwd_kv_tile, bwd_q_tile, tiles, max_tiles, hdr);
+hipError_t launch_sched(const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k,
+                        int tile, int mode, bool causal, int fwd_kv_tile, int bwd_q_tile,
+                        int* tiles, int max_tiles, uint32_t* hdr, hipStream_t stream) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, cu_q, cu_k, nseq, total_q,
+                     total_k, tile, mode, causal ? 1 : 0, fwd_kv_tile, bwd_q_tile, tiles,
+                     max_tiles, hdr);
   return hipGetLastError();
 }
 

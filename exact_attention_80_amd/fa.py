@@ -39,6 +39,10 @@ _SIGS = {
     "fa_varlen_fwd": ([_p] * 6 + [_i] * 6 + [_f, _i, _p, _sz, _p], _i),
     "fa_varlen_bwd_workspace_size": ([_i] * 7, _sz),
     "fa_varlen_bwd": ([_p] * 10 + [_i] * 6 + [_f, _i, _i, _p, _sz, _p], _i),
+    "fa_varlen_qk_fwd_workspace_size": ([_i] * 7, _sz),
+    "fa_varlen_qk_fwd": ([_p] * 7 + [_i] * 8 + [_f, _i, _p, _sz, _p], _i),
+    "fa_varlen_qk_bwd_workspace_size": ([_i] * 8, _sz),
+    "fa_varlen_qk_bwd": ([_p] * 11 + [_i] * 8 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_workspace_error": ([_p, _sz, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
     "fa_timing_begin": ([], _i),
     "fa_timing_end": ([ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)], _i),
@@ -206,6 +210,83 @@ def varlen_bwd(q, k, v, o, lse, do, cu_seqlens, causal: bool = False,
                               Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
                               int(deterministic), ws.data_ptr(), ws.numel(), _stream()),
            "fa_varlen_bwd")
+    return dq, dk, dv
+
+
+def varlen_qk_fwd_workspace(nseq: int, Tq: int, Tk: int, Hq: int, Hkv: int, d: int,
+                            causal: bool, device) -> torch.Tensor | None:
+    return _workspace(_lib.fa_varlen_qk_fwd_workspace_size(nseq, Tq, Tk, Hq, Hkv, d, int(causal)),
+                      device)
+
+
+def varlen_qk_bwd_workspace(nseq: int, Tq: int, Tk: int, Hq: int, Hkv: int, d: int, causal: bool,
+                            deterministic: int | bool, device) -> torch.Tensor:
+    n = _lib.fa_varlen_qk_bwd_workspace_size(nseq, Tq, Tk, Hq, Hkv, d, int(causal),
+                                             int(deterministic))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _cu_pair(cu_q, cu_k):
+    nseq = _cu(cu_q, 0)
+    _need(cu_k, "cu_seqlens_k", (nseq + 1,), torch.int32)
+    return nseq
+
+
+def varlen_qk_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
+                  softmax_scale: float | None = None, max_seqlen_q: int = 0,
+                  max_seqlen_k: int = 0, workspace: torch.Tensor | None = None):
+    """Packed forward with separate query and key lengths per sequence:
+    q [Tq,Hq,d], k/v [Tk,Hkv,d], cu_seqlens_q / cu_seqlens_k int32 [nseq+1] on
+    the device -> (o [Tq,Hq,d], lse [Hq,Tq]).  Causal masks are aligned
+    bottom-right (query i sees key j iff j <= i + Lk - Lq)."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    _need(q, "q", (Tq, Hq, d))
+    _need(k, "k", (Tk, Hkv, d))
+    _need(v, "v", (Tk, Hkv, d))
+    nseq = _cu_pair(cu_seqlens_q, cu_seqlens_k)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    ws = workspace
+    if ws is None:
+        ws = varlen_qk_fwd_workspace(nseq, Tq, Tk, Hq, Hkv, d, causal, q.device)
+    _check(_lib.fa_varlen_qk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                 nseq, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
+                                 _scale(d, softmax_scale), int(causal), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream()),
+           "fa_varlen_qk_fwd")
+    return o, lse
+
+
+def varlen_qk_bwd(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
+                  softmax_scale: float | None = None, deterministic: int | bool = False,
+                  max_seqlen_q: int = 0, max_seqlen_k: int = 0,
+                  workspace: torch.Tensor | None = None):
+    """Packed backward with separate query and key lengths
+    -> (dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]); deterministic 0 or 1."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    _need(q, "q", (Tq, Hq, d))
+    _need(k, "k", (Tk, Hkv, d))
+    _need(v, "v", (Tk, Hkv, d))
+    _need(o, "o", (Tq, Hq, d))
+    _need(do, "do", (Tq, Hq, d))
+    _need(lse, "lse", (Hq, Tq), torch.float32)
+    nseq = _cu_pair(cu_seqlens_q, cu_seqlens_k)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = workspace
+    if ws is None:
+        ws = varlen_qk_bwd_workspace(nseq, Tq, Tk, Hq, Hkv, d, causal, deterministic, q.device)
+    _check(_lib.fa_varlen_qk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                 nseq, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
+                                 _scale(d, softmax_scale), int(causal), int(deterministic),
+                                 ws.data_ptr(), ws.numel(), _stream()),
+           "fa_varlen_qk_bwd")
     return dq, dk, dv
 
 

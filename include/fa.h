@@ -34,11 +34,16 @@
  *    word (fa_workspace_error), not by the return value.
  *  - d (head dimension) is 64 or 128.  Hq must be a positive multiple of Hkv;
  *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
- *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2);
- *    queries and keys always have the same length.
+ *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2)
+ *    when queries and keys have the same length.  The fa_varlen_qk_* calls
+ *    take separate query and key lengths per sequence (Lq, Lk; the
+ *    decode-shaped batches of [FA4B] 3.3.2): the queries are the last Lq
+ *    positions of the Lk-token context, so the mask is aligned bottom-right,
+ *    hiding key j from query i when j > i + Lk - Lq.  A query that sees no key
+ *    (Lq > Lk, or Lk = 0) gets O = 0, LSE = -inf and dQ = 0.
  *  - softmax_scale multiplies q.k before the softmax (typically 1/sqrt(d)).
  *  - LSE_i = ln sum_j exp(softmax_scale * q_i.k_j)  ([FA2] "Core method" 1:
- *    the only statistic the backward needs).
+ *    the only statistic the backward needs), over the keys query i sees.
  *  - stream is a hipStream_t passed as void* (NULL = default stream).  Every
  *    call is asynchronous on that stream; argument errors are detected on the
  *    host and returned before anything is launched.
@@ -158,6 +163,39 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
                   const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
                   int Hq, int Hkv, int d, float softmax_scale, int causal,
                   int deterministic, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- packed batches with separate query and key lengths ------------------
+ * q/o/dout/dq [total_q, Hq, d] and lse [Hq, total_q]; k/v/dk/dv
+ * [total_k, Hkv, d].  Sequence s has queries cu_seqlens_q[s] .. [s+1]-1 and
+ * keys cu_seqlens_k[s] .. [s+1]-1; both arrays are DEVICE int32 with nseq+1
+ * entries, validated on the device (first 0, last total_q / total_k,
+ * non-decreasing; a violation sets FA_DEVERR_BAD_CU_SEQLENS).  A sequence may
+ * have Lq = 0 or Lk = 0; total_q and total_k must be positive.  Causal masks
+ * are bottom-right aligned (see the conventions above).  The scheduling kernel
+ * orders the tiles by their cost under that mask, longest first ([FA4B]
+ * 3.3.2).  max_seqlen_q / max_seqlen_k are hints (>= 0, 0 if unknown).  With
+ * cu_seqlens_q == cu_seqlens_k these calls compute exactly what
+ * fa_varlen_fwd / fa_varlen_bwd compute. */
+size_t fa_varlen_qk_fwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
+                                       int d, int causal);
+
+int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                     int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                     int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* deterministic must be 0 or 1 (2 returns FA_ERR_UNSUPPORTED); the size query
+ * returns 0 for invalid sizes or modes. */
+size_t fa_varlen_qk_bwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
+                                       int d, int causal, int deterministic);
+
+int fa_varlen_qk_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                     int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                     int Hkv, int d, float softmax_scale, int causal, int deterministic, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /*
  * Debug/test helper: synchronises `stream`, reads the device error word that

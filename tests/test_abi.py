@@ -34,6 +34,12 @@ def lib():
     L.fa_varlen_fwd_workspace_size.restype = sz
     L.fa_varlen_bwd_workspace_size.argtypes = [i] * 7
     L.fa_varlen_bwd_workspace_size.restype = sz
+    L.fa_varlen_qk_fwd.argtypes = [p] * 7 + [i] * 8 + [f, i, p, sz, p]
+    L.fa_varlen_qk_bwd.argtypes = [p] * 11 + [i] * 8 + [f, i, i, p, sz, p]
+    L.fa_varlen_qk_fwd_workspace_size.argtypes = [i] * 7
+    L.fa_varlen_qk_fwd_workspace_size.restype = sz
+    L.fa_varlen_qk_bwd_workspace_size.argtypes = [i] * 8
+    L.fa_varlen_qk_bwd_workspace_size.restype = sz
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_workspace_error.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_uint32)]
@@ -48,7 +54,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_fwd_workspace_size",
+    for n in ("fa_fwd", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_varlen_qk_fwd",
+              "fa_varlen_qk_bwd", "fa_fwd_workspace_size",
               "fa_bwd_workspace_size", "fa_status_string", "fa_workspace_error"):
         assert n in names
 
@@ -136,6 +143,42 @@ def test_varlen_rejects_bad_arguments(lib):
     assert lib.fa_varlen_bwd_workspace_size(3, 300, 2, 2, 64, 1, 2) == 0
     assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 2, P, wb,
                              None) == UNSUPPORTED
+
+
+def test_varlen_qk_sizes_and_bad_arguments(lib):
+    # equal lengths: the same workspace as the single-offset calls
+    assert (lib.fa_varlen_qk_fwd_workspace_size(3, 300, 300, 2, 2, 64, 1)
+            == lib.fa_varlen_fwd_workspace_size(3, 300, 2, 2, 64, 1))
+    for det in (0, 1):
+        assert (lib.fa_varlen_qk_bwd_workspace_size(3, 300, 300, 4, 2, 64, 1, det)
+                == lib.fa_varlen_bwd_workspace_size(3, 300, 4, 2, 64, 1, det))
+    # the backward workspace grows with the query side (dQ accumulator, D, LSE)
+    # and, when a group is split, with the key side (dK/dV partials)
+    small = lib.fa_varlen_qk_bwd_workspace_size(3, 30, 3000, 2, 2, 128, 1, 0)
+    big = lib.fa_varlen_qk_bwd_workspace_size(3, 3000, 3000, 2, 2, 128, 1, 0)
+    assert small >= 30 * 2 * 128 * 4 and big - small >= (3000 - 30) * 2 * 128 * 4
+    assert lib.fa_varlen_qk_bwd_workspace_size(3, 300, 0, 2, 2, 64, 1, 0) == 0
+    assert lib.fa_varlen_qk_bwd_workspace_size(3, 300, 400, 2, 2, 64, 1, 2) == 0
+    wf = lib.fa_varlen_qk_fwd_workspace_size(3, 30, 400, 2, 2, 64, 1)
+    args = [P] * 7 + [3, 30, 400, 0, 0, 2, 2, 64, 0.1, 1, P, wf, None]
+    a = list(args); a[6] = None                    # cu_seqlens_k
+    assert lib.fa_varlen_qk_fwd(*a) == INVALID
+    a = list(args); a[5] = None                    # cu_seqlens_q
+    assert lib.fa_varlen_qk_fwd(*a) == INVALID
+    a = list(args); a[9] = 0                       # total_k
+    assert lib.fa_varlen_qk_fwd(*a) == INVALID
+    a = list(args); a[11] = -1                     # max_seqlen_k
+    assert lib.fa_varlen_qk_fwd(*a) == INVALID
+    a = list(args); a[18] = 8                      # workspace too small
+    assert lib.fa_varlen_qk_fwd(*a) == WORKSPACE
+    wb = lib.fa_varlen_qk_bwd_workspace_size(3, 30, 400, 2, 2, 64, 1, 1)
+    bargs = [P] * 11 + [3, 30, 400, 0, 0, 2, 2, 64, 0.1, 1, 1, P, wb, None]
+    b = list(bargs); b[10] = None                  # cu_seqlens_k
+    assert lib.fa_varlen_qk_bwd(*b) == INVALID
+    b = list(bargs); b[21] = 2                     # partial-sum mode is dense-only
+    assert lib.fa_varlen_qk_bwd(*b) == UNSUPPORTED
+    b = list(bargs); b[23] = wb - 1
+    assert lib.fa_varlen_qk_bwd(*b) == WORKSPACE
 
 
 def test_workspace_error_rejects_null(lib):
