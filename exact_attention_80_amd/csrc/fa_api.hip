@@ -157,17 +157,30 @@ int check_dims(long tokens, int Hq, int Hkv, int d, int causal, float scale) {
 // workspace layouts
 
 struct FwdLayout {
-  size_t hdr = 0, tiles = 0, total = 0;
+  size_t hdr = 0, tiles = 0, split_base = 0, part_o = 0, part_ml = 0, total = 0;
   int max_tiles = 0;
+  int max_split = 0;  // partial slots for the chunks of split query tiles
 };
 
-FwdLayout fwd_layout(bool varlen, int nseq, long T) {
+// T: query tokens, Tk: key tokens.  A split tile has at most
+// ceil(key tiles / 32) chunks of 32 key tiles of 64 keys, so the chunks of
+// all sequences number at most Tk / 2048 + 2 nseq.
+FwdLayout fwd_layout(bool varlen, int nseq, long T, long Tk, int Hq, int d) {
   FwdLayout l;
   if (!varlen) return l;
-  l.max_tiles = (int)(T / fa::fwd_tile_rows() + nseq);
+  l.max_split = (int)(Tk / (fa::fwd_tile_keys() * 32) + 2L * nseq + 1);
+  l.max_tiles = (int)(T / fa::fwd_tile_rows() + nseq + l.max_split);
   l.hdr = 0;
-  l.tiles = align_up(fa::kHdrWords * 4);
-  l.total = l.tiles + align_up((size_t)l.max_tiles * 2 * 4);
+  size_t off = align_up(fa::kHdrWords * 4);
+  l.tiles = off;
+  off += align_up((size_t)l.max_tiles * 2 * 4);
+  l.split_base = off;
+  off += align_up((size_t)(nseq + 1) * 4);
+  l.part_o = off;
+  off += align_up((size_t)l.max_split * Hq * 32 * d * 4);
+  l.part_ml = off;
+  off += align_up((size_t)l.max_split * Hq * 32 * 2 * 4);
+  l.total = off;
   return l;
 }
 
@@ -265,7 +278,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
     return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
   if ((st = check_dims(Tk, Hq, Hkv, d, causal, scale))) return st;
-  const FwdLayout lay = fwd_layout(varlen, nseq, T);
+  const FwdLayout lay = fwd_layout(varlen, nseq, T, Tk, Hq, d);
   if (ws_bytes < lay.total || (lay.total > 0 && !ws))
     return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*fwd_workspace_size()");
   if (lay.total > 0 && (st = check_ptr(ws, "ws"))) return st;
@@ -294,12 +307,16 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
     uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, lay.hdr));
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
     const long tk = timing_start(4, s);
+    int* split_base = reinterpret_cast<int*>(at(ws, lay.split_base));
     e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, br, 0, causal != 0, fa::fwd_tile_keys(),
-                         fa::kBwdBQ, tiles, lay.max_tiles, hdr, s);
+                         fa::kBwdBQ, tiles, lay.max_tiles, split_base, lay.max_split, hdr, s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
     p.cu_seqlens_k = cu_k;
+    p.split_base = split_base;
+    p.part_o = reinterpret_cast<float*>(at(ws, lay.part_o));
+    p.part_ml = reinterpret_cast<float*>(at(ws, lay.part_ml));
     p.tiles = tiles;
     p.hdr = hdr;
     grid = (long)lay.max_tiles * Hq;
@@ -313,6 +330,12 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
   e = fa::launch_fwd(p, d, causal != 0, varlen, (int)grid, s);
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
+  if (varlen) {
+    const long tc = timing_start(5, s);
+    e = fa::launch_fwd_combine(p, d, nseq, s);
+    timing_stop(tc, s);
+    if (e != hipSuccess) return hip_fail(e, "forward combine launch");
+  }
   return FA_OK;
 }
 
@@ -390,8 +413,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
     tk = timing_start(4, s);
     e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, fa::kBwdBC, deterministic ? 2 : 1,
-                         causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles, hdr,
-                         s);
+                         causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles,
+                         nullptr, 0, hdr, s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
@@ -484,9 +507,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
                                     int causal) {
-  (void)Hq; (void)Hkv; (void)d; (void)causal;
-  if (nseq <= 0 || total_tokens <= 0) return 0;
-  return fwd_layout(true, nseq, total_tokens).total;
+  (void)Hkv; (void)causal;
+  if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || (d != 64 && d != 128)) return 0;
+  return fwd_layout(true, nseq, total_tokens, total_tokens, Hq, d).total;
 }
 
 int fa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -522,9 +545,9 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, co
 
 size_t fa_varlen_qk_fwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
                                        int d, int causal) {
-  (void)total_k; (void)Hq; (void)Hkv; (void)d; (void)causal;
-  if (nseq <= 0 || total_q <= 0) return 0;
-  return fwd_layout(true, nseq, total_q).total;
+  (void)Hkv; (void)causal;
+  if (nseq <= 0 || total_q <= 0 || total_k <= 0 || Hq <= 0 || (d != 64 && d != 128)) return 0;
+  return fwd_layout(true, nseq, total_q, total_k, Hq, d).total;
 }
 
 int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -40,6 +40,16 @@ constexpr int kHdrTicket = 1;    // deterministic backward work-item ticket
 constexpr int kHdrCount = 2;     // number of valid entries in the tile list
 constexpr int kHdrWords = 64;    // 256 bytes
 
+// Forward work items that are one chunk of a split query tile carry this bit
+// (the low 20 bits are the chunk index).
+constexpr int kSplitItem = 1 << 30;
+// Key tiles per chunk of a split forward query tile with nt key tiles: 32,
+// or more when a row has over 32768 key tiles (at most 1024 chunks).
+__host__ __device__ __forceinline__ int fwd_split_chunk_tiles(int nt) {
+  const int c = (nt + 1023) / 1024;
+  return c > 32 ? c : 32;
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -387,6 +397,9 @@ struct FwdParams {
   const int* cu_seqlens_k;  // varlen only: key offsets (the same array when Lq == Lk)
   const int* tiles;       // varlen only: (sequence, q-tile) pairs in schedule order
   const uint32_t* hdr;    // varlen only: workspace header (error word, tile count)
+  const int* split_base;  // varlen only: first partial slot per sequence (nseq + 1)
+  float* part_o;          // varlen only: [slot, Hq, 32, d] unnormalised partial outputs
+  float* part_ml;         // varlen only: [slot, Hq, 32, 2] partial (reference max, row sum)
   int B, N, Hq, Hkv, G;   // dense: N is the sequence length
   int T;                  // total query tokens (varlen LSE layout [Hq, T])
   int nq;                 // dense: number of query tiles per sequence

@@ -19,7 +19,8 @@
 //    read from the row-major V tile with transposed LDS reads, in the key
 //    order the P fragment already has) and is divided by the row sum once at
 //    the end; only LSE = ln(sum exp) is saved;
-//  * causal: key tiles wholly above a wave's rows are skipped, the mask is
+//  * causal: key tiles wholly above a wave's rows are skipped (as are all
+//    tiles for a wave whose rows lie past the sequence end), the mask is
 //    applied only on tiles that straddle the diagonal or the sequence end;
 //    a packed sequence with Lq queries and Lk keys aligns the diagonal
 //    bottom-right (query i sees key j iff j <= i + Lk - Lq, the decode-shaped
@@ -45,6 +46,8 @@ struct WorkItem {
   int h;          // query head
   int qtile;
   bool valid;
+  bool split;     // one chunk of a split query tile (varlen only)
+  int chunk;
 };
 
 template <bool CAUSAL, bool VARLEN>
@@ -58,7 +61,10 @@ __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
     w.valid = e < count && (p.hdr[kHdrErr] & kErrBadCu) == 0;
     if (!w.valid) return w;
     w.b = p.tiles[2 * e];
-    w.qtile = p.tiles[2 * e + 1];
+    const int v = p.tiles[2 * e + 1];
+    w.split = (v & kSplitItem) != 0;
+    w.chunk = v & 0xFFFFF;
+    w.qtile = w.split ? -1 : v;  // a split chunk belongs to the last query tile
     w.seq_start = p.cu_seqlens[w.b];
     w.seq_len = p.cu_seqlens[w.b + 1] - w.seq_start;
     w.k_start = p.cu_seqlens_k[w.b];
@@ -91,6 +97,8 @@ __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
     w.k_start = w.seq_start;
     w.k_len = p.N;
     w.off = 0;
+    w.split = false;
+    w.chunk = 0;
     w.valid = true;
   }
   return w;
@@ -106,8 +114,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   constexpr int STAGES = kFwdStages;             // K/V tiles in flight or in use
   __shared__ __attribute__((aligned(16))) char kv_s[STAGES][KT::kBytes + VT::kBytes];
 
-  const WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
+  WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
   if (!wi.valid) return;
+  if (VARLEN && wi.split) wi.qtile = (wi.seq_len - 1) / BR;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,7 +150,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   }
 
   const int kv_end = CAUSAL ? max(0, min(klen, q0 + BR + off)) : klen;
-  const int nt = (kv_end + kBC - 1) / kBC;
+  const int nt_all = (kv_end + kBC - 1) / kBC;
+  // key tiles jb .. jb + nt - 1 (a split chunk covers its own range)
+  const bool split = VARLEN && wi.split;
+  const int ct = fwd_split_chunk_tiles(nt_all);
+  const int jb = split ? wi.chunk * ct : 0;
+  const int nt = split ? min(ct, nt_all - jb) : nt_all;
 
   // ---- direct global->LDS copy of one K and one V tile.  Rows past the
   // sequence end arrive as zeros (buffer range check); their scores are
@@ -153,8 +167,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   TileCopy<VT, NW> vcopy;
   kcopy.init(kv_bytes, CH + 1, wave, lane, [](int, int pc) { return pc < CH ? pc : -1; });
   vcopy.init(kv_bytes, VST, wave, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
-  auto issue_tile = [&](int j) {
-    char* kt = kv_s[j % STAGES];
+  auto issue_tile = [&](int u) {  // the u-th tile of this item, key tile jb + u
+    char* kt = kv_s[u % STAGES];
+    const int j = jb + u;
     const uint32_t range = tile_range(j * kBC, klen, kv_bytes, D * 2);
     kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * kv_row, range));
     vcopy.issue(kt + KT::kBytes, make_rsrc(vbase + (long)j * kBC * kv_row, range));
@@ -251,21 +266,46 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < nt) issue_tile(t);
-  for (int j = 0; j < nt; ++j) {
-    const int newer = min(nt - 1 - j, STAGES - 2);  // tiles issued after j
+  for (int u = 0; u < nt; ++u) {
+    const int j = jb + u;
+    const int newer = min(nt - 1 - u, STAGES - 2);  // tiles issued after this one
     if (newer >= 2) wait_vmem_leave<2 * kCopies>();
     else if (newer == 1) wait_vmem_leave<kCopies>();
     else wait_vmem();
-    lds_barrier();  // tile j landed for every wave; tile j-1's buffer is free
-    if (j + STAGES - 1 < nt) issue_tile(j + STAGES - 1);
-    const char* kt = kv_s[j % STAGES];
-    compute_tile(j, kt, kt + KT::kBytes);
+    lds_barrier();  // tile u landed for every wave; tile u-1's buffer is free
+    if (u + STAGES - 1 < nt) issue_tile(u + STAGES - 1);
+    const char* kt = kv_s[u % STAGES];
+    // a wave whose rows are all past the sequence end, or (causal) all above
+    // this tile's first key, would only add exact zeros: it skips the tile
+    // (it still copies and meets every barrier)
+    const bool live = wq0 < wi.seq_len && (!CAUSAL || j * kBC <= wq0 + 31 + off);
+    if (live) compute_tile(j, kt, kt + KT::kBytes);
   }
 
   // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2;
   // a row that saw no key (l = 0) stores O = 0 and LSE = -inf
   const float ltot = halves_sum(lsum);
   if (!q_ok) return;
+  if (split) {
+    // a chunk of a split tile (only wave 0 holds live rows): the unscaled
+    // O~, its reference max and row sum go to this chunk's partial slot
+    const long slot = (long)p.split_base[wi.b] + wi.chunk;
+    const long row = (slot * p.Hq + wi.h) * 32 + l32;
+    float* po = p.part_o + row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(po + d0) = f32x4{oacc[db][4 * g + 0], oacc[db][4 * g + 1],
+                                                   oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+      }
+    if (half == 0) {
+      p.part_ml[2 * row] = m_ref;
+      p.part_ml[2 * row + 1] = ltot;
+    }
+    return;
+  }
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
   bf16* orow = p.o + ((long)wi.seq_start + qi) * q_row + (long)wi.h * D;
 #pragma unroll
@@ -287,6 +327,58 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   }
 }
 
+// Merge of the chunks of split query tiles: per row, M = max_c m_c,
+// l = sum_c 2^(m_c - M) l_c, O = sum_c 2^(m_c - M) O~_c / l, LSE =
+// (M + log2 l) ln 2, with the chunks taken in ascending order (the same result
+// on every run).  The chunks' m_c are reference maxima of the online softmax
+// ([FA2] "Core method" 1): rescaling partial sums to a common maximum is the
+// same step that merges key tiles inside one workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p, int br) {
+  // nothing to merge when the scheduler rejected the offsets or the lists
+  // overflowed (split_base may then be stale)
+  if (p.hdr[kHdrErr] & (kErrBadCu | kErrTileOverflow)) return;
+  const int s = blockIdx.x / p.Hq;
+  const int h = blockIdx.x - s * p.Hq;
+  const int base = p.split_base[s];
+  const int n = p.split_base[s + 1] - base;
+  if (n == 0) return;
+  const int q_start = p.cu_seqlens[s];
+  const int lq = p.cu_seqlens[s + 1] - q_start;
+  const int q0 = ((lq - 1) / br) * br;  // first row of the split (last) tile
+  const int live = lq - q0;             // at most 32
+  constexpr int CPR = D / 8;            // 8-float chunks per row
+  const int t = threadIdx.x;
+  for (int w = t; w < 32 * CPR; w += 256) {
+    const int r = w / CPR, c8 = (w - r * CPR) * 8;
+    if (r >= live) continue;
+    float M = -INFINITY;
+    for (int c = 0; c < n; ++c)
+      M = fmaxf(M, p.part_ml[2 * (((long)(base + c) * p.Hq + h) * 32 + r)]);
+    float l = 0.f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n; ++c) {
+      const long row = ((long)(base + c) * p.Hq + h) * 32 + r;
+      const float mc = p.part_ml[2 * row];
+      if (mc == -INFINITY) continue;  // this chunk saw no key of the row
+      const float wgt = fast_exp2(mc - M);
+      l += wgt * p.part_ml[2 * row + 1];
+      const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o + row * D + c8);
+      o0 += wgt * po[0];
+      o1 += wgt * po[1];
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const long tok = (long)q_start + q0 + r;
+    u32x4 w4;
+    w4[0] = pack2_bf16(o0[0] * inv, o0[1] * inv);
+    w4[1] = pack2_bf16(o0[2] * inv, o0[3] * inv);
+    w4[2] = pack2_bf16(o1[0] * inv, o1[1] * inv);
+    w4[3] = pack2_bf16(o1[2] * inv, o1[3] * inv);
+    *reinterpret_cast<u32x4*>(p.o + tok * ((long)p.Hq * D) + (long)h * D + c8) = w4;
+    if (c8 == 0) p.lse[(long)h * p.T + tok] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
 template <int D, int NW, bool CAUSAL, bool VARLEN>
 hipError_t launch_fwd_t(const FwdParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VARLEN>), dim3(grid), dim3(NW * 64), 0, stream, p);
@@ -296,6 +388,18 @@ hipError_t launch_fwd_t(const FwdParams& p, int grid, hipStream_t stream) {
 }  // namespace
 
 int fwd_tile_rows() { return kFwdWaves * 32; }
+
+hipError_t launch_fwd_combine(const FwdParams& p, int d, int nseq, hipStream_t stream) {
+  const long grid = (long)nseq * p.Hq;
+  if (grid <= 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+                       kFwdWaves * 32);
+  else
+    hipLaunchKernelGGL(fwd_combine_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+                       kFwdWaves * 32);
+  return hipGetLastError();
+}
 int fwd_tile_keys() { return kBC; }
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,

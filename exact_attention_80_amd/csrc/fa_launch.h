@@ -67,8 +67,15 @@ hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float s
 //   mode 0: forward query tiles, longest first
 //   mode 1: backward key tiles, longest first
 //   mode 2: backward key tiles, deterministic order (key tiles of a sequence last-first)
+// Mode 0 also writes split_base (nseq + 1 ints, first partial slot per
+// sequence) and flags an overflow when more than max_split chunks are needed.
 hipError_t launch_sched(const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k,
                         int tile, int mode, bool causal, int fwd_kv_tile, int bwd_q_tile,
-                        int* tiles, int max_tiles, uint32_t* hdr, hipStream_t stream);
+                        int* tiles, int max_tiles, int* split_base, int max_split, uint32_t* hdr,
+                        hipStream_t stream);
+
+// Forward combine of split tiles: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
+// per row, in ascending chunk order; one workgroup per (sequence, query head).
+hipError_t launch_fwd_combine(const FwdParams& p, int d, int nseq, hipStream_t stream);
 
 }  // namespace fa

@@ -299,7 +299,7 @@ def workspace_error(ws: torch.Tensor) -> int:
     return int(bits.value)
 
 
-TIMING_KINDS = ("fwd", "bwd_main", "bwd_pre", "bwd_post", "sched")
+TIMING_KINDS = ("fwd", "bwd_main", "bwd_pre", "bwd_post", "sched", "fwd_combine")
 
 
 def timing_begin() -> None:

@@ -138,7 +138,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* max_seqlen: a hint (an upper bound on any sequence length, or 0 if unknown);
  * it must be >= 0 and is otherwise unused, since the scheduling kernel reads
- * the lengths from cu_seqlens itself.  total_tokens = T = cu_seqlens[nseq]. */
+ * the lengths from cu_seqlens itself.  total_tokens = T = cu_seqlens[nseq].
+ * The forward workspace holds the header, the tile list and the partial
+ * results of split query tiles: a sequence whose last query tile has at most
+ * 32 queries and more than 32 key tiles of 64 keys has that tile split into
+ * chunks of 32 key tiles that run as separate work items ([FA2] "Core
+ * method" 2: parallelism over the sequence), merged exactly afterwards by a
+ * second kernel.  0 for invalid sizes. */
 size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
                                     int causal);
 
@@ -216,10 +222,12 @@ int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* 
  *   kind 0: forward kernel;  kind 1: backward main kernel;
  *   kind 2: backward preprocess (D = rowsum(dO o O), zeroing);
  *   kind 3: backward post (dQ conversion or partial-tile sum, split dK/dV sum);
- *   kind 4: variable-length scheduler.
+ *   kind 4: variable-length scheduler;
+ *   kind 5: variable-length forward combine (merges the key chunks of split
+ *           query tiles).
  * counts / ms must each point to FA_TIMING_KINDS elements (or be NULL).
  * Events are created lazily and reused; nothing is allocated on the device. */
-#define FA_TIMING_KINDS 5
+#define FA_TIMING_KINDS 6
 int fa_timing_begin(void);
 int fa_timing_end(int* counts, float* ms);
 

@@ -79,6 +79,50 @@ def test_varlen_qk_parity(fa, case, causal, det):
     assert np.all(o[empty] == 0.0) and np.all(dq[empty] == 0.0)
 
 
+SPLIT_CASES = [
+    # last query tile with <= 32 rows against more than 32 key tiles: split
+    # into chunks of 32 key tiles and merged by the combine kernel
+    ([1, 17, 32, 33, 257, 288, 289], [5000, 5000, 2049, 5000, 3000, 2100, 2100], 4, 2, 128),
+    ([1, 3], [70000, 4100], 2, 1, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"n{len(c[0])}d{c[4]}")
+def test_split_query_tiles(fa, case, causal):
+    lq, lk, Hq, Hkv, d = case
+    x, _, _, outs = run_qk(fa, lq, lk, Hq, Hkv, d, causal, 0, seed=7)
+    o, lse = to_host(outs[0]), to_host(outs[1])
+    sc = scale_for(d)
+    ro, rlse = ora.varlen_qk_forward(x["q"], x["k"], x["v"], x["cu_seqlens_q"],
+                                     x["cu_seqlens_k"], sc, causal)
+    errs = dict(o_excess=o_excess(o, ro), lse=lse_error(lse, rlse))
+    rdq, rdk, rdv = ora.varlen_qk_backward(x["q"], x["k"], x["v"], x["do"], x["cu_seqlens_q"],
+                                           x["cu_seqlens_k"], sc, causal)
+    dq, dk, dv = (to_host(a) for a in outs[2:])
+    errs.update(dq=rel_fro(dq, rdq), dk=rel_fro(dk, rdk), dv=rel_fro(dv, rdv))
+    say(f"errors {errs}")
+    assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE
+    assert errs["dq"] <= TOL_GRAD and errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD
+
+
+def test_split_tiles_in_equal_length_batches(fa):
+    """The single-offset packed forward splits too (a 2305-token sequence
+    ends with a one-row tile over 37 key tiles); repeated calls agree bit
+    for bit."""
+    import torch
+    lengths = [2305, 40, 4097]
+    x = inputs.varlen_inputs(lengths, 2, 2, 128, seed=2)
+    t = {n: to_dev(x[n]) for n in ("q", "k", "v")}
+    cu = torch.from_numpy(x["cu_seqlens"]).to("cuda")
+    o, lse = fa.varlen_fwd(t["q"], t["k"], t["v"], cu, causal=True, softmax_scale=scale_for(128))
+    o2, lse2 = fa.varlen_fwd(t["q"], t["k"], t["v"], cu, causal=True, softmax_scale=scale_for(128))
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    ro, rlse = ora.varlen_forward(x["q"], x["k"], x["v"], x["cu_seqlens"], scale_for(128), True)
+    say(f"o_excess {o_excess(to_host(o), ro):.3f} lse {lse_error(to_host(lse), rlse):.2e}")
+    assert o_excess(to_host(o), ro) <= 1.0 and lse_error(to_host(lse), rlse) <= TOL_LSE
+
+
 def test_equal_lengths_match_the_single_offset_call(fa):
     """With cu_seqlens_q == cu_seqlens_k the separate-length entry points run
     the same kernels on the same schedule: bit-identical forward and
