@@ -626,14 +626,31 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* part, b
   constexpr int PITCH = D + 4;    // LDS row pitch in floats
   __shared__ float tile[BQ * PITCH];
   const int t = threadIdx.x;
-  const int i = blockIdx.x % nq;
-  const int bh = blockIdx.x / nq;  // b * Hq + h
+  // heaviest query tiles (most key tiles) first, every head's at once
+  const int nbh = gridDim.x / nq;
+  const int i = CAUSAL ? nq - 1 - (int)(blockIdx.x / nbh) : (int)(blockIdx.x / nbh);
+  const int bh = blockIdx.x % nbh;  // b * Hq + h
   const int jn = CAUSAL ? i / (BC / BQ) + 1 : nkv;
   const float* src = part + ((long)bh * head_pairs + pair_index<CAUSAL>(i, 0, nkv)) * F;
   f32x4 acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < jn; ++j) {
+  // four partial tiles per step: 4 V independent 16-byte loads in flight
+  // per thread, added in ascending j afterwards (the order never changes)
+  int j = 0;
+  for (; j + 4 <= jn; j += 4) {
+    f32x4 x[4][V];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        x[u][v] = *reinterpret_cast<const f32x4*>(src + (long)(j + u) * F + 4 * (t + 256 * v));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += x[u][v];
+  }
+  for (; j < jn; ++j) {
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] += *reinterpret_cast<const f32x4*>(src + (long)j * F + 4 * (t + 256 * v));
   }
