@@ -191,8 +191,8 @@ def run_decode(args):
 
     Hq, Hkv, d = 32, 4, 128
     det = args.dq_mode
-    if det == 2:
-        print("bench.py: the partial-tile dQ reduction is dense-only", file=sys.stderr)
+    if det >= 2:
+        print("bench.py: the partial-tile dQ reductions are dense-only", file=sys.stderr)
         sys.exit(2)
     lq, lk = inputs.qk_lengths()
     x = inputs.varlen_qk_inputs(lq, lk, Hq, Hkv, d, seed=0)
@@ -294,8 +294,10 @@ def main():
     ap.add_argument("--Hkv", type=int, default=0)
     ap.add_argument("--d", type=int, default=128)
     ap.add_argument("--non-causal", action="store_true")
-    ap.add_argument("--dq-mode", type=int, default=0, choices=(0, 1, 2),
-                    help="dQ reduction: 0 fp32 atomics, 1 semaphore-ordered, 2 partial tiles")
+    ap.add_argument("--dq-mode", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="dQ reduction: 0 fp32 atomics, 1 semaphore-ordered, 2 partial tiles "
+                         "summed by a second kernel, 3 partial tiles summed by the last "
+                         "contributor")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
     ap.add_argument("--traffic-file", default=TRAFFIC_FILE,
@@ -383,7 +385,7 @@ def main():
     if args.extra:
         o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
         this_ms = (ms_bwd + ms_pre + ms_post) / max(1, n_bwd)
-        for mode in (0, 1, 2):
+        for mode in (0, 1, 2, 3):
             if mode == det:
                 continue
             wsd = fa.bwd_workspace(x["q"], x["k"], causal, mode)
@@ -420,7 +422,8 @@ def main():
         "config": {
             "workload": f"{'causal' if causal else 'non-causal'} self-attention forward+backward, "
                         f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}, "
-                        f"{('atomic', 'semaphore-ordered', 'partial-tile')[det]} dQ reduction",
+                        f"{('atomic', 'semaphore-ordered', 'partial-tile', 'fused partial-tile')[det]} "
+                        f"dQ reduction",
             "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
             "deterministic": det,
         },

@@ -225,14 +225,14 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, long Tk, int H
   l.lse2 = off;
   off += align_up((size_t)T * Hq * 4);
   l.dq_acc = off;
-  if (deterministic == 2) {
+  if (deterministic >= 2) {
     l.head_pairs = fa::bwd_partial_pairs(N, causal);
     l.dq_part = off;
     off += align_up((size_t)B * Hq * l.head_pairs * fa::kBwdBQ * d * 4);
   } else {
     off += align_up((size_t)T * Hq * d * 4);
   }
-  if (deterministic == 1) {
+  if (deterministic == 1 || deterministic == 3) {  // semaphores, or arrival counters
     if (varlen) {
       l.sem_slots = (int)(T / fa::kBwdBQ + nseq + 1);
       l.sem_count = (long)Hq * l.sem_slots;
@@ -353,10 +353,10 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
   if ((st = check_dims(Tk, Hq, Hkv, d, causal, scale))) return st;
-  if (deterministic < 0 || deterministic > 2)
-    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1 or 2");
-  if (varlen && deterministic == 2)
-    return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 (partial-sum dQ) is dense-only");
+  if (deterministic < 0 || deterministic > 3)
+    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1, 2 or 3");
+  if (varlen && deterministic >= 2)
+    return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 or 3 (partial-tile dQ) is dense-only");
   const BwdLayout lay =
       bwd_layout(varlen, B, N, nseq, T, Tk, Hq, Hkv, d, deterministic, causal != 0);
   if (!ws || ws_bytes < lay.total)
@@ -368,7 +368,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, 0));
   float* dvec = reinterpret_cast<float*>(at(ws, lay.dvec));
-  float* dq_acc = deterministic == 2 ? nullptr : reinterpret_cast<float*>(at(ws, lay.dq_acc));
+  float* dq_acc = deterministic >= 2 ? nullptr : reinterpret_cast<float*>(at(ws, lay.dq_acc));
   int* sem = reinterpret_cast<int*>(at(ws, lay.sem));
   long tk = timing_start(2, s);
   float* lse2 = reinterpret_cast<float*>(at(ws, lay.lse2));
@@ -392,7 +392,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   p.dk_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dk_part)) : nullptr;
   p.dv_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dv_part)) : nullptr;
   p.sem = sem;
-  p.dq_part = deterministic == 2 ? reinterpret_cast<float*>(at(ws, lay.dq_part)) : nullptr;
+  p.dq_part = deterministic >= 2 ? reinterpret_cast<float*>(at(ws, lay.dq_part)) : nullptr;
+  p.dq = static_cast<fa::bf16*>(dq);
   p.head_pairs = lay.head_pairs;
   p.hdr = hdr;
   p.B = B;
@@ -434,7 +435,13 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
   tk = timing_start(3, s);
-  if (deterministic == 2) {
+  if (deterministic == 3) {
+    // dQ is written by the main kernel; only split dK/dV partials remain
+    if (lay.S > 1)
+      e = fa::launch_bwd_post(nullptr, nullptr, 0, scale, p.dk_part, p.dv_part,
+                              static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
+                              Tk * Hkv * d, lay.S, s);
+  } else if (deterministic == 2) {
     e = fa::launch_bwd_dq_reduce(p.dq_part, static_cast<fa::bf16*>(dq), B, N, Hq, d, causal != 0,
                                  p.nq, p.nkv, lay.head_pairs, scale, s);
     if (e == hipSuccess && lay.S > 1)
@@ -490,7 +497,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
-  if (deterministic < 0 || deterministic > 2) return 0;
+  if (deterministic < 0 || deterministic > 3) return 0;
   return bwd_layout(false, B, N, 0, (long)B * N, (long)B * N, Hq, Hkv, d, deterministic,
                     causal != 0).total;
 }

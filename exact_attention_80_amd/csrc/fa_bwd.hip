@@ -20,6 +20,11 @@
 //    Workgroups take their work items from an atomic ticket in that same
 //    descending order, so every workgroup a writer waits for already runs and
 //    the causal walk (diagonal first) never stalls on its first write.
+//    A third way (fused partial sums) needs neither atomics on dQ nor a
+//    second kernel: every workgroup stores its fp32 partial tile, counts
+//    itself in with one atomic per tile once its stores are complete, and the
+//    last contributor of a query tile sums all partial tiles in ascending
+//    key-tile order and writes bf16 dQ (deterministic by construction).
 //  * post: dQ = bf16(scale * dQ_acc); split subgroups' dK/dV partials are
 //    summed in a fixed order.
 // A packed sequence may have Lq queries and Lk keys (the decode-shaped
@@ -75,6 +80,8 @@ __device__ __forceinline__ int ds_off(int key, int s) {
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   constexpr bool DET = DQM == kDqOrdered;
+  constexpr bool FUSED = DQM == kDqFused;
+  constexpr bool PARTS = DQM == kDqPartial || FUSED;  // partial tiles in dq_part
   using L = BwdLds<D>;
   constexpr int ST = L::STRIDE;
   using KT = typename L::KT;
@@ -89,6 +96,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char ds_s0[L::dsBytes];
   __shared__ __attribute__((aligned(16))) char ds_s1[L::dsBytes];
   __shared__ int sh_ticket;
+  __shared__ int sh_last[4];  // fused mode: "this workgroup completes item t" (t mod 4)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,6 +200,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   const int i_start = CAUSAL ? max(0, key0 - it.off) / BQ : 0;
   const int nsteps = max(0, it.nq - i_start);
   const int nitems = GS * nsteps;
+  // query tile of step u of a head's walk: from the diagonal upwards, or in
+  // the fused mode from the top down (every key tile then reaches a given
+  // query tile at about the same step, which spreads the last-contributor
+  // reductions over the workgroups)
+  auto step_tile = [&](int u) { return (FUSED && CAUSAL) ? it.nq - 1 - u : i_start + u; };
 
   // direct copy of one query tile's Q, dO rows (rows past the sequence end
   // read as zeros) and LSE, D values
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   qcopy.init(q_row * 2, ST, wave, lane, [](int row, int pc) { return QT::slot_chunk(row, pc); });
   auto issue_item = [&](int item, char* qd, char* dod, char* std_) {
     const int hh = item / nsteps;
-    const int i = i_start + (item - hh * nsteps);
+    const int i = step_tile(item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
     const long tok = (long)it.q_start + q0;
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // dQ of item `item` from its dS^T (all waves' rows), reduced into dq_acc
   auto dq_item = [&](int item, const char* dss) {
     const int hh = item / nsteps;
-    const int i = i_start + (item - hh * nsteps);
+    const int i = step_tile(item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
     f32x4 acc[NQB];
@@ -289,6 +302,18 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       float* dst = p.dq_part + slot * (BQ * D) + ((wave * NQB) * 64 + lane) * 4;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) *reinterpret_cast<f32x4*>(dst + qb * 256) = acc[qb];
+      return;
+    }
+    if (FUSED) {
+      // the same tile, stored coherently for the whole device (sc1): another
+      // workgroup, possibly on another XCD, sums it once the count says so
+      const long slot = ((long)it.seq * p.Hq + h) * p.head_pairs + pair_index<CAUSAL>(i, it.jt, it.nkv);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          p.dq_part + slot * (BQ * D), (short)0, BQ * D * 4, 0x00020000);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        __builtin_amdgcn_raw_buffer_store_b128(as_u32x4(acc[qb]), rs,
+                                               (((wave * NQB + qb) * 64 + lane) * 16), 0, kCoherent);
       return;
     }
     if (!DET) {
@@ -364,7 +389,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   auto compute_item = [&](int item, const char* qs, const char* dos, const char* sts,
                           char* dsd) {
     const int hh = item / nsteps;
-    const int i = i_start + (item - hh * nsteps);
+    const int i = step_tile(item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
 
@@ -450,6 +475,70 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
   };
 
+  // Fused mode.  count_item (thread 0): the partial tile of `item` is stored
+  // by every wave; one relaxed device atomic counts it in, and the workgroup
+  // that brings the count to the query tile's number of key tiles finishes
+  // that tile.  reduce_item (all threads): sum of the partial tiles in
+  // ascending key-tile order (coherent loads), times the scale, into bf16 dQ.
+  auto count_item = [&](int item) {
+    const int hh = item / nsteps;
+    const int i = step_tile(item - hh * nsteps);
+    const int h = h0 + hh;
+    const int jn = CAUSAL ? min(it.nkv, (i * BQ + BQ - 1) / BC + 1) : it.nkv;
+    const int old = __hip_atomic_fetch_add(p.sem + ((long)it.seq * p.Hq + h) * p.nq + i, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last[item & 3] = old == jn - 1;
+  };
+  auto reduce_item = [&](int item) {
+    const int hh = item / nsteps;
+    const int i = step_tile(item - hh * nsteps);
+    const int h = h0 + hh;
+    const int jn = CAUSAL ? min(it.nkv, (i * BQ + BQ - 1) / BC + 1) : it.nkv;
+    constexpr int F = BQ * D;                  // floats per partial tile
+    constexpr int V = F / (4 * NT);            // 16-byte pieces per thread per tile
+    const long slot0 = ((long)it.seq * p.Hq + h) * p.head_pairs + pair_index<CAUSAL>(i, 0, it.nkv);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        p.dq_part + slot0 * F, (short)0, jn * F * 4, 0x00020000);
+    f32x4 acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int j = 0;
+    for (; j + 4 <= jn; j += 4) {
+      f32x4 x[4][V];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          x[u][v] = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(
+              rs, ((j + u) * F + 4 * (tid + NT * v)) * 4, 0, kCoherent));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] += x[u][v];
+    }
+    for (; j < jn; ++j)
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        acc[v] += as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(
+            rs, (j * F + 4 * (tid + NT * v)) * 4, 0, kCoherent));
+    // fragment order: float4 f4 = (w NQB + qb) 64 + lane holds rows
+    // 16 ((w / DB16) NQB + qb) + 4 (lane / 16) + 0..3 of column 16 (w % DB16) + lane % 16
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int f4 = tid + NT * v;
+      const int ln = f4 & 63, wq = f4 >> 6;
+      const int w = wq / NQB, qb = wq - (wq / NQB) * NQB;
+      const int row0 = 16 * ((w / DB16) * NQB + qb) + 4 * (ln >> 4);
+      const int col = 16 * (w % DB16) + (ln & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = i * BQ + row0 + r;
+        if (q < it.q_len)
+          p.dq[((long)it.q_start + q) * q_row + (long)h * D + col] = (bf16)(acc[v][r] * p.scale);
+      }
+    }
+  };
+
   // Per item: one barrier (the item's copies landed and the previous item's
   // dS^T is complete), then the previous item's dQ products and atomics,
   // then this item's S, dP, dV, dK and its dS^T (into the other buffer).
@@ -458,7 +547,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // were issued after them, so those stay in flight.
   auto wait_copies = [&](int item) {
     if (DQM == kDqAtomic && item >= 2) wait_vmem_leave<4 * NQB>();
-    else if (DQM == kDqPartial && item >= 2) wait_vmem_leave<NQB>();
+    else if (PARTS && item >= 2) wait_vmem_leave<NQB>();
     else wait_vmem();
     lds_barrier();
   };
@@ -467,6 +556,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   if (nitems > 0) issue_item(0, q_s0, do_s0, st_s0);
   for (int item = 0; item < nitems; ++item) {
     wait_copies(item);
+    if (FUSED) {
+      // the partial tile of item-3 is complete in every wave (its stores
+      // were issued before copies this wait covered); item-4 was counted
+      // before this barrier
+      if (item >= 4 && sh_last[item & 3]) reduce_item(item - 4);
+      if (item >= 3 && tid == 0) count_item(item - 3);
+    }
     const bool odd = item & 1;
     char* qs = odd ? q_s1 : q_s0;
     char* dos = odd ? do_s1 : do_s0;
@@ -480,6 +576,18 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   if (nitems > 0) {
     lds_barrier();  // the last item's dS^T is complete
     dq_item(nitems - 1, (nitems - 1) & 1 ? ds_s1 : ds_s0);
+  }
+  if (FUSED && nitems > 0) {
+    wait_vmem();    // every partial tile of this workgroup is stored
+    lds_barrier();  // ... by every wave; item nitems-4 was counted
+    const int t0 = max(0, nitems - 4);
+    if (nitems >= 4 && sh_last[t0 & 3]) reduce_item(t0);
+    __syncthreads();  // sh_last[t0 & 3] is reused below
+    if (tid == 0)
+      for (int t = max(0, nitems - 3); t < nitems; ++t) count_item(t);
+    __syncthreads();
+    for (int t = max(0, nitems - 3); t < nitems; ++t)
+      if (sh_last[t & 3]) reduce_item(t);
   }
 
   // ---------------- dK = scale * sum dS^T Q, dV = sum P^T dO for this wave's keys
@@ -514,6 +622,8 @@ hipError_t launch_bwd_mode(const BwdParams& p, int mode, int grid, hipStream_t s
   if (mode == kDqOrdered) return launch_bwd_t<D, CAUSAL, VARLEN, kDqOrdered>(p, grid, stream);
   if (mode == kDqPartial && !VARLEN)
     return launch_bwd_t<D, CAUSAL, false, kDqPartial>(p, grid, stream);
+  if (mode == kDqFused && !VARLEN)
+    return launch_bwd_t<D, CAUSAL, false, kDqFused>(p, grid, stream);
   return launch_bwd_t<D, CAUSAL, VARLEN, kDqAtomic>(p, grid, stream);
 }
 

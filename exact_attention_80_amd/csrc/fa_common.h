@@ -56,6 +56,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 b) { return __builtin_bit_cast(u32x4, b); }
+__device__ __forceinline__ u32x4 as_u32x4(f32x4 x) { return __builtin_bit_cast(u32x4, x); }
+__device__ __forceinline__ f32x4 as_f32x4(u32x4 x) { return __builtin_bit_cast(f32x4, x); }
+
+// cache-policy argument of the buffer load / store builtins that makes the
+// access coherent across the whole device (the sc1 bit on gfx950): stores
+// reach the level every XCD reads, loads read from it
+constexpr int kCoherent = 16;
 
 // Pack 8 fp32 values (round to nearest even) into one MFMA operand.
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3,
@@ -435,8 +442,9 @@ struct BwdParams {
   bf16* dv;
   float* dk_part;         // [S, Tk, Hkv, d] fp32 when S > 1
   float* dv_part;
-  int* sem;               // dQ tile semaphores (ordered mode)
-  float* dq_part;         // per-(query tile, key tile) dQ partial tiles (partial-sum mode)
+  int* sem;               // dQ tile semaphores (ordered mode) or arrival counters (fused mode)
+  float* dq_part;         // per-(query tile, key tile) dQ partial tiles (partial-sum modes)
+  bf16* dq;               // dQ output (fused partial-sum mode writes it directly)
   long head_pairs;        // partial tiles per (sequence, query head)
   uint32_t* hdr;          // workspace header
   const int* cu_seqlens;  // varlen only: query offsets

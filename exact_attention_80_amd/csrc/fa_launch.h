@@ -17,6 +17,7 @@ constexpr int kBwdBC = kBwdWaves * 32;
 constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
 constexpr int kDqOrdered = 1;  // semaphore-ordered adds into dq_acc (bit-reproducible)
 constexpr int kDqPartial = 2;  // plain stores of every partial tile, summed by bwd_dq_reduce
+constexpr int kDqFused = 3;    // partial tiles summed by the last workgroup to finish its own
 
 // Index of the partial dQ tile of (query tile i, key tile j) inside its
 // (sequence, head): the query tiles' key-tile counts laid end to end (causal:
@@ -44,7 +45,9 @@ hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, flo
                           int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream);
 
 // mode: dQ reduction across key tiles (0 fp32 atomics, 1 semaphore-ordered
-// adds, 2 partial tiles summed by launch_bwd_dq_reduce; 2 is dense-only)
+// adds, 2 partial tiles summed by launch_bwd_dq_reduce, 3 partial tiles summed
+// inside the kernel by the last contributor of each query tile; 2 and 3 are
+// dense-only)
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int mode, int grid,
                       hipStream_t stream);
 

@@ -126,7 +126,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
 
     deterministic selects the dQ reduction across key tiles: 0 (False) fp32
     atomics, 1 (True) semaphore-ordered adds, 2 partial tiles summed in a fixed
-    order by a second kernel; 1 and 2 are bit-reproducible."""
+    order by a second kernel, 3 partial tiles summed in a fixed order by the
+    last workgroup to contribute to each query tile; 1, 2 and 3 are
+    bit-reproducible."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     _need(q, "q", (B, N, Hq, d))

@@ -107,10 +107,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /* ---- dense backward ----------------------------------------------------- */
 
 /* Workspace bytes fa_bwd needs (D = rowsum(dO o O), the fp32 dQ accumulator or,
- * for deterministic == 2, the fp32 partial dQ tiles (32 x d floats per pair of
- * a 32-row query tile and a 256-key tile that meet: about 2.2 GB for causal
- * B=2, Hq=16, N=8192, d=128), ordering semaphores, split dK/dV partials).
- * 0 when the sizes or the mode are invalid. */
+ * for deterministic == 2 or 3, the fp32 partial dQ tiles (32 x d floats per
+ * pair of a 32-row query tile and a 256-key tile that meet: about 2.2 GB for
+ * causal B=2, Hq=16, N=8192, d=128), ordering semaphores or arrival counters,
+ * split dK/dV partials).  0 when the sizes or the mode are invalid. */
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic);
 
@@ -125,8 +125,13 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
  * semaphores when deterministic == 1 ([FA4B] 3.2, 3.3.1), or, when
  * deterministic == 2, stored as one fp32 tile per (query tile, key tile)
  * pair and summed in ascending key-tile order by a second kernel (no atomics;
- * dense layout only).  Modes 1 and 2 make dQ/dK/dV bit-identical from run to
- * run.  dK/dV never use atomics.  Any other value: FA_ERR_INVALID_ARG.
+ * dense layout only), or, when deterministic == 3, stored the same way
+ * (coherent for the whole device) and summed in the same order inside the
+ * main kernel by the last workgroup to contribute to each query tile, which
+ * writes dQ itself (one counting atomic per tile; dense layout only).
+ * Modes 1, 2 and 3 make dQ/dK/dV bit-identical from run to run (and the
+ * partial-tile modes 2 and 3 give the same dQ).  dK/dV never use atomics.
+ * Any other value: FA_ERR_INVALID_ARG.
  * Outputs dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] bf16.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -163,7 +168,7 @@ size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv,
                                     int causal, int deterministic);
 
 /* Backward over a packed batch; semantics as fa_bwd, per sequence.
- * deterministic must be 0 or 1 (2 returns FA_ERR_UNSUPPORTED). */
+ * deterministic must be 0 or 1 (2 or 3 returns FA_ERR_UNSUPPORTED). */
 int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
@@ -191,8 +196,8 @@ int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float
                      int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
                      void* stream);
 
-/* deterministic must be 0 or 1 (2 returns FA_ERR_UNSUPPORTED); the size query
- * returns 0 for invalid sizes or modes. */
+/* deterministic must be 0 or 1 (2 or 3 returns FA_ERR_UNSUPPORTED); the size
+ * query returns 0 for invalid sizes or modes. */
 size_t fa_varlen_qk_bwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
                                        int d, int causal, int deterministic);
 

@@ -97,7 +97,7 @@ def bwd(lib, ws=P, ws_bytes=None, det=0, d=64, dq=P, B=1, N=128, Hq=2, Hkv=2):
 def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws_bytes=16) == WORKSPACE
-    assert bwd(lib, det=3) == INVALID
+    assert bwd(lib, det=4) == INVALID
     assert bwd(lib, det=-1) == INVALID
     assert bwd(lib, dq=None) == INVALID
     assert bwd(lib, d=80) == UNSUPPORTED
@@ -120,7 +120,10 @@ def test_workspace_sizes(lib):
     assert abs((part - fast) - (pairs_bytes - B * N * Hq * d * 4)) <= 1024
     full = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 0, 2)
     assert full >= B * Hq * nq * ((N + 255) // 256) * 32 * d * 4
-    assert lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 3) == 0
+    # fused partial-sum mode: the same partial tiles plus one counter per query tile
+    fused = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 3)
+    assert 0 <= fused - part <= B * Hq * nq * 4 + 512
+    assert lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 4) == 0
     assert lib.fa_bwd_workspace_size(B, N, 3, 2, d, 1, 0) == 0
     vf = lib.fa_varlen_fwd_workspace_size(5, 4000, Hq, Hkv, d, 1)
     vb = lib.fa_varlen_bwd_workspace_size(5, 4000, Hq, Hkv, d, 1, 1)
@@ -142,6 +145,8 @@ def test_varlen_rejects_bad_arguments(lib):
     # the partial-sum dQ reduction is dense-only
     assert lib.fa_varlen_bwd_workspace_size(3, 300, 2, 2, 64, 1, 2) == 0
     assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 2, P, wb,
+                             None) == UNSUPPORTED
+    assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 3, P, wb,
                              None) == UNSUPPORTED
 
 

@@ -71,7 +71,7 @@ def test_dense_parity(fa, shape, causal):
     check_against_oracle(x, outs, causal, d)
 
 
-@pytest.mark.parametrize("mode", [1, 2], ids=["ordered", "partial"])
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["ordered", "partial", "fused"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_dense_parity_deterministic(fa, causal, mode):
     x, _, outs = run_dense(fa, 2, 451, 6, 2, 128, causal, seed=3, deterministic=mode)
@@ -82,16 +82,39 @@ PARTIAL_CASES = [(1, 128, 2, 2, 64), (1, 1, 2, 1, 128), (1, 17, 3, 1, 64), (2, 3
                  (1, 1024, 4, 2, 128), (1, 777, 2, 2, 64)]
 
 
+@pytest.mark.parametrize("mode", [2, 3], ids=["partial", "fused"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", PARTIAL_CASES, ids=lambda s: "x".join(map(str, s)))
-def test_dense_parity_partial_sums(fa, shape, causal):
-    """dQ summed from per-(query tile, key tile) partial tiles (mode 2)."""
+def test_dense_parity_partial_sums(fa, shape, causal, mode):
+    """dQ summed from per-(query tile, key tile) partial tiles, by a second
+    kernel (mode 2) or by the last contributor inside the kernel (mode 3)."""
     B, N, Hq, Hkv, d = shape
-    x, _, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=7, deterministic=2)
+    x, _, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=7, deterministic=mode)
     check_against_oracle(x, outs, causal, d)
 
 
-@pytest.mark.parametrize("mode", [1, 2], ids=["ordered", "partial"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 513, 4, 2, 128), (1, 777, 2, 2, 64), (1, 1, 2, 1, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_partial_tile_modes_agree_bit_for_bit(fa, shape, causal):
+    """Modes 2 and 3 add the same dQ partial tiles in the same order, so dQ
+    agrees bit for bit.  (dK and dV agree too without a causal mask; with it,
+    mode 3 walks the query tiles from the top, which changes the order of
+    their register sums, so they only agree within rounding.)"""
+    import torch
+    B, N, Hq, Hkv, d = shape
+    x, t, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=9, deterministic=2)
+    g3 = fa.bwd(t["q"], t["k"], t["v"], outs[0], outs[1], t["do"], causal=causal,
+                softmax_scale=scale_for(d), deterministic=3)
+    assert torch.equal(outs[2].view(torch.int16), g3[0].view(torch.int16))
+    for a, b in zip(outs[3:], g3[1:]):
+        if causal:
+            assert rel_fro(to_host(b), to_host(a)) <= 1e-2
+        else:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["ordered", "partial", "fused"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 513, 4, 2, 128), (1, 640, 2, 1, 64)],
                          ids=lambda s: "x".join(map(str, s)))

@@ -163,7 +163,7 @@ def headline(fa):
     return prob, refs
 
 
-@pytest.mark.parametrize("det", [0, 1, 2], ids=["atomic", "ordered", "partial"])
+@pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])
 def test_headline_whole_heads(headline, det):
     prob, refs = headline
     grads = prob.backward(det)
@@ -172,7 +172,7 @@ def test_headline_whole_heads(headline, det):
     check_dv_sum(grads[2], prob.t["do"], 1)
 
 
-@pytest.mark.parametrize("mode", [1, 2], ids=["ordered", "partial"])
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["ordered", "partial", "fused"])
 def test_headline_deterministic_bit_identical(headline, mode):
     import torch
     prob, _ = headline
@@ -198,7 +198,7 @@ def test_mha_2k(fa, d, causal):
 
 # ---- long context B=1 H=16 N=16384/32768 ----------------------------------------
 
-@pytest.mark.parametrize("det", [0, 1, 2], ids=["atomic", "ordered", "partial"])
+@pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])
 @pytest.mark.parametrize("N", [16384, 32768])
 def test_long_context(fa, N, det):
     prob = dense_problem(fa, 1, N, 16, 16, 128, True, seed=2)
@@ -211,7 +211,7 @@ def test_long_context(fa, N, det):
 
 # ---- GQA / MQA B=2 Hq=32 Hkv=4/1 N=8192 ---------------------------------------------
 
-@pytest.mark.parametrize("det", [0, 1, 2], ids=["atomic", "ordered", "partial"])
+@pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])
 @pytest.mark.parametrize("hkv", [4, 1])
 def test_gqa_mqa(fa, hkv, det):
     prob = dense_problem(fa, 2, 8192, 32, hkv, 128, True, seed=3)
