@@ -146,7 +146,8 @@ int check_dims(long tokens, int Hq, int Hkv, int d, int causal, float scale) {
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(FA_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64, 128 or 256");
   if (tokens * (long)Hq * d >= (1L << 31) * 16L)
     return fail(FA_ERR_UNSUPPORTED, "tensor too large");
   if (tokens > (1L << 30)) return fail(FA_ERR_UNSUPPORTED, "too many tokens");
@@ -169,7 +170,7 @@ FwdLayout fwd_layout(bool varlen, int nseq, long T, long Tk, int Hq, int d) {
   FwdLayout l;
   if (!varlen) return l;
   l.max_split = (int)(Tk / (fa::fwd_tile_keys() * 32) + 2L * nseq + 1);
-  l.max_tiles = (int)(T / fa::fwd_tile_rows() + nseq + l.max_split);
+  l.max_tiles = (int)(T / fa::fwd_tile_rows(d) + nseq + l.max_split);
   l.hdr = 0;
   size_t off = align_up(fa::kHdrWords * 4);
   l.tiles = off;
@@ -213,10 +214,10 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, long Tk, int H
   const int G = Hq / Hkv;
   long units;
   if (varlen) {
-    l.max_tiles = (int)(Tk / fa::kBwdBC + nseq);
-    units = (long)Hkv * (Tk / fa::kBwdBC + 1);
+    l.max_tiles = (int)(Tk / fa::bwd_tile_keys(d) + nseq);
+    units = (long)Hkv * (Tk / fa::bwd_tile_keys(d) + 1);
   } else {
-    units = (long)B * Hkv * cdiv(N, fa::kBwdBC);
+    units = (long)B * Hkv * cdiv(N, fa::bwd_tile_keys(d));
   }
   l.S = choose_split(units, G);
   size_t off = align_up(fa::kHdrWords * 4);
@@ -300,7 +301,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
   p.T = (int)T;
   p.sched = sched_mode();
   p.c = scale * fa::kLog2e;
-  const int br = fa::fwd_tile_rows();
+  const int br = fa::fwd_tile_rows(d);
   long grid;
   hipError_t e;
   if (varlen) {
@@ -357,6 +358,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1, 2 or 3");
   if (varlen && deterministic >= 2)
     return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 or 3 (partial-tile dQ) is dense-only");
+  if (d == 256 && deterministic >= 2)
+    return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 or 3 (partial-tile dQ) needs d <= 128");
   const BwdLayout lay =
       bwd_layout(varlen, B, N, nseq, T, Tk, Hq, Hkv, d, deterministic, causal != 0);
   if (!ws || ws_bytes < lay.total)
@@ -413,7 +416,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (varlen) {
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
     tk = timing_start(4, s);
-    e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, fa::kBwdBC, deterministic ? 2 : 1,
+    e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, fa::bwd_tile_keys(d),
+                         deterministic ? 2 : 1,
                          causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles,
                          nullptr, 0, hdr, s);
     timing_stop(tk, s);
@@ -423,7 +427,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     p.tiles = tiles;
     grid = (long)lay.max_tiles * Hkv * lay.S;
   } else {
-    p.nkv = (int)cdiv(N, fa::kBwdBC);
+    p.nkv = (int)cdiv(N, fa::bwd_tile_keys(d));
     p.nq = (int)cdiv(N, fa::kBwdBQ);
     grid = (long)B * Hkv * lay.S * p.nkv;
   }
@@ -498,6 +502,7 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
   if (deterministic < 0 || deterministic > 3) return 0;
+  if (d == 256 && deterministic >= 2) return 0;
   return bwd_layout(false, B, N, 0, (long)B * N, (long)B * N, Hq, Hkv, d, deterministic,
                     causal != 0).total;
 }
@@ -515,7 +520,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 size_t fa_varlen_fwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv, int d,
                                     int causal) {
   (void)Hkv; (void)causal;
-  if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || (d != 64 && d != 128)) return 0;
+  if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
   return fwd_layout(true, nseq, total_tokens, total_tokens, Hq, d).total;
 }
 
@@ -553,7 +558,8 @@ int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o, co
 size_t fa_varlen_qk_fwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
                                        int d, int causal) {
   (void)Hkv; (void)causal;
-  if (nseq <= 0 || total_q <= 0 || total_k <= 0 || Hq <= 0 || (d != 64 && d != 128)) return 0;
+  if (nseq <= 0 || total_q <= 0 || total_k <= 0 || Hq <= 0 || (d != 64 && d != 128 && d != 256))
+    return 0;
   return fwd_layout(true, nseq, total_q, total_k, Hq, d).total;
 }
 

@@ -57,13 +57,17 @@ constexpr int BC = kBwdBC;
 // 512 + 16384 + 16384 bytes.
 template <int D>
 struct BwdLds {
+  static constexpr int BCD = bwd_tile_keys(D);       // keys per workgroup
   static constexpr int CH = D / 8;
-  static constexpr int STRIDE = D == 128 ? 20 : 12;  // pitch 320 or 192 bytes
-  using KT = SwzTile<BC, CH, STRIDE>;                // K tile [BC][D]
+  // row pitch 16 (mod 64) dwords (320, 192 or 576 bytes); the d = 256 K tile
+  // uses 544 bytes so that K, the double-buffered Q / dO and dS^T fit in LDS
+  static constexpr int STRIDE = D == 256 ? 36 : (D == 128 ? 20 : 12);
+  static constexpr int KSTRIDE = D == 256 ? 34 : STRIDE;
+  using KT = SwzTile<BCD, CH, KSTRIDE>;              // K tile [BC][D]
   using QT = SwzTile<BQ, CH, STRIDE>;                // Q or dO tile [BQ][D]
   static constexpr int statBytes = 2 * BQ * 4;       // LSE[BQ] then D[BQ]
   static constexpr int dsPitch = BQ * 2;             // dS^T row: 32 bf16
-  static constexpr int dsBytes = BC * dsPitch;
+  static constexpr int dsBytes = BCD * dsPitch;
 };
 
 // byte offset of the 8-byte slot holding dS^T[key][4s .. 4s+3].  The slot
@@ -78,12 +82,16 @@ __device__ __forceinline__ int ds_off(int key, int s) {
 }
 
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
-__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
+  constexpr int NW = bwd_waves(D);  // waves of 32 keys (shadows the d <= 128 defaults)
+  constexpr int NT = NW * 64;
+  constexpr int BC = NW * 32;
   constexpr bool DET = DQM == kDqOrdered;
   constexpr bool FUSED = DQM == kDqFused;
   constexpr bool PARTS = DQM == kDqPartial || FUSED;  // partial tiles in dq_part
   using L = BwdLds<D>;
   constexpr int ST = L::STRIDE;
+  constexpr int KST = L::KSTRIDE;
   using KT = typename L::KT;
   using QT = typename L::QT;
   __shared__ __attribute__((aligned(16))) char k_s[KT::kBytes];
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // ---------------- K tile -> LDS (direct), V rows of this wave -> registers
   const bf16* kseq = p.k + (long)it.k_start * kv_row + (long)it.hkv * D;
   const bf16* vseq = p.v + (long)it.k_start * kv_row + (long)it.hkv * D;
-  dma_swz_tile<KT, ST, NW>(k_s, kseq, kv_row, key0, klast, wave, lane);
+  dma_swz_tile<KT, KST, NW>(k_s, kseq, kv_row, key0, klast, wave, lane);
   bf16x8 vf[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
@@ -232,14 +240,20 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   };
 
   // dQ tile (BQ x D) of an item = dS (BQ x BC) K (BC x D) with 16x16x32
-  // products: wave w owns the 16-column block dblk of dQ for NQB 16-row
-  // blocks (both for d = 128, one for d = 64), over all BC keys, so no
-  // partial sums are exchanged and every wave adds its own block.
+  // products: wave w owns NCB 16-column blocks of dQ, from dblk on, for NQB
+  // 16-row blocks from qb0 on (d = 128: one column block, both row blocks;
+  // d = 64: one of each; d = 256: four column blocks, both row blocks), over
+  // all BC keys, so no partial sums are exchanged and every wave adds its own
+  // blocks.
   constexpr int DB16 = D / 16;               // 16-column blocks of dQ
-  constexpr int NQB = (2 * DB16) / NW;       // 16-row blocks per wave
-  static_assert(NQB >= 1 && NQB * NW == 2 * DB16, "dQ work split");
-  const int dblk = wave % DB16;
-  const int qb0 = (wave / DB16) * NQB;
+  constexpr int UPW = (2 * DB16) / NW;       // (row block, column block) units per wave
+  constexpr int NQB = UPW >= 2 ? 2 : 1;      // 16-row blocks per wave
+  constexpr int NCB = UPW / NQB;             // 16-column blocks per wave
+  static_assert(NQB * NCB * NW == 2 * DB16, "dQ work split");
+  static_assert(NCB == 1 || !PARTS, "partial-tile modes use one column block per wave");
+  constexpr int CG = DB16 / NCB;             // column groups
+  const int dblk = (wave % CG) * NCB;
+  const int qb0 = (wave / CG) * NQB;
 
   // Per-lane LDS byte offsets.  Every operand read below is one of these
   // bases plus a compile-time constant (the tile swizzle only permutes chunks
@@ -257,8 +271,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   //   K columns 16 dblk + 4(L16%4):  k_tr[ld] + 32 ks pitch
   //   dS^T slots of queries 16qb + 4(L16%4):  ds_tr[qb][ld] + 2048 ks
   const int rk = 8 * g16 + (L16 >> 2);
-  const int k_tr[2] = {KT::off(rk, 16 * dblk + 4 * (L16 & 3)),
-                       KT::off(rk + 4, 16 * dblk + 4 * (L16 & 3))};
+  int k_tr[NCB][2];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    k_tr[c][0] = KT::off(rk, 16 * (dblk + c) + 4 * (L16 & 3));
+    k_tr[c][1] = KT::off(rk + 4, 16 * (dblk + c) + 4 * (L16 & 3));
+  }
   int ds_tr[NQB][2];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -272,30 +290,48 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const int i = step_tile(item - hh * nsteps);
     const int h = h0 + hh;
     const int q0 = i * BQ;
-    f32x4 acc[NQB];
+    f32x4 acc[NCB * NQB];  // [c * NQB + qb]
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NCB * NQB; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     // operands of key step ks+1 are read while step ks's products run
-    bf16x8 ob[2], oa[2][NQB];
-    auto load_ks = [&](int ks, bf16x8& b, bf16x8 (&a)[NQB]) {
+    bf16x8 ob[2][NCB], oa[2][NQB];
+    auto load_ks = [&](int ks, bf16x8 (&b)[NCB], bf16x8 (&a)[NQB]) {
       const int ko = 32 * ks * KT::kPitch;
-      b = cat8(ld_lds_tr8(k_s + k_tr[0] + ko), ld_lds_tr8(k_s + k_tr[1] + ko));
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        b[c] = cat8(ld_lds_tr8(k_s + k_tr[c][0] + ko), ld_lds_tr8(k_s + k_tr[c][1] + ko));
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
         a[qb] = cat8(ld_lds_tr8(dss + ds_tr[qb][0] + 2048 * ks),
                      ld_lds_tr8(dss + ds_tr[qb][1] + 2048 * ks));
     };
-    load_ks(0, ob[0], oa[0]);
+    if constexpr (NCB == 1) {
+      load_ks(0, ob[0], oa[0]);
 #pragma unroll
-    for (int ks = 0; ks < BC / 32; ++ks) {
-      if (ks + 1 < BC / 32) load_ks(ks + 1, ob[(ks + 1) & 1], oa[(ks + 1) & 1]);
+      for (int ks = 0; ks < BC / 32; ++ks) {
+        if (ks + 1 < BC / 32) load_ks(ks + 1, ob[(ks + 1) & 1], oa[(ks + 1) & 1]);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ks & 1][qb], ob[ks & 1], acc[qb],
-                                                          0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int qb = 0; qb < NQB; ++qb)
+          acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ks & 1][qb], ob[ks & 1][0],
+                                                            acc[qb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // several column blocks (d = 256): one operand set at a time keeps the
+      // register file for the dK, dV accumulators
+#pragma unroll
+      for (int ks = 0; ks < BC / 32; ++ks) {
+        load_ks(ks, ob[0], oa[0]);
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            acc[c * NQB + qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                oa[0][qb], ob[0][c], acc[c * NQB + qb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // acc[qb][r] = dQ[q = q0 + 16(qb0 + qb) + 4 g16 + r][d = 16 dblk + L16]
+    // acc[c NQB + qb][r] = dQ[q = q0 + 16(qb0 + qb) + 4 g16 + r][d = 16 (dblk + c) + L16]
     if (DQM == kDqPartial) {
       // the tile in fragment order: 4 NQB floats per lane, NQB 16-byte stores
       const long slot = ((long)it.seq * p.Hq + h) * p.head_pairs + pair_index<CAUSAL>(i, it.jt, it.nkv);
@@ -334,11 +370,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       asm volatile("" : "+v"(vo));
       const int row_bytes = (int)q_row * 4;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-              acc[qb][r], rsrc, vo + (16 * qb + r) * row_bytes, 0, 0);
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                acc[c * NQB + qb][r], rsrc, vo + (16 * qb + r) * row_bytes + 64 * c, 0, 0);
     } else {
       float* dq_base = p.dq_acc + (long)it.q_start * q_row + (long)h * D + dblk * 16 + L16;
       // ordered reduction: writers of a dQ tile apply in descending key-tile order
@@ -371,14 +409,16 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
       __syncthreads();
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
-          if (q < it.q_len)
-            __hip_atomic_fetch_add(dq_base + (long)q * q_row, acc[qb][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
+            if (q < it.q_len)
+              __hip_atomic_fetch_add(dq_base + (long)q * q_row + 16 * c, acc[c * NQB + qb][r],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
       // every add of this workgroup has been performed before the release
       wait_vmem();
       __syncthreads();
@@ -546,7 +586,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // or stores of the dQ issued in the previous item (4 NQB or NQB per wave)
   // were issued after them, so those stay in flight.
   auto wait_copies = [&](int item) {
-    if (DQM == kDqAtomic && item >= 2) wait_vmem_leave<4 * NQB>();
+    if (DQM == kDqAtomic && item >= 2) wait_vmem_leave<4 * NQB * NCB>();
     else if (PARTS && item >= 2) wait_vmem_leave<NQB>();
     else wait_vmem();
     lds_barrier();
@@ -613,17 +653,20 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
 hipError_t launch_bwd_t(const BwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, VARLEN, DQM>), dim3(grid), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, VARLEN, DQM>), dim3(grid), dim3(bwd_waves(D) * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_mode(const BwdParams& p, int mode, int grid, hipStream_t stream) {
   if (mode == kDqOrdered) return launch_bwd_t<D, CAUSAL, VARLEN, kDqOrdered>(p, grid, stream);
-  if (mode == kDqPartial && !VARLEN)
-    return launch_bwd_t<D, CAUSAL, false, kDqPartial>(p, grid, stream);
-  if (mode == kDqFused && !VARLEN)
-    return launch_bwd_t<D, CAUSAL, false, kDqFused>(p, grid, stream);
+  if constexpr (D != 256) {  // the partial-tile modes take d <= 128
+    if (mode == kDqPartial && !VARLEN)
+      return launch_bwd_t<D, CAUSAL, false, kDqPartial>(p, grid, stream);
+    if (mode == kDqFused && !VARLEN)
+      return launch_bwd_t<D, CAUSAL, false, kDqFused>(p, grid, stream);
+  }
   return launch_bwd_t<D, CAUSAL, VARLEN, kDqAtomic>(p, grid, stream);
 }
 
@@ -797,6 +840,7 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* part, b
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int mode, int grid,
                       hipStream_t stream) {
+  if (d == 256) return launch_bwd_d<256>(p, causal, varlen, mode, grid, stream);
   if (d == 128) return launch_bwd_d<128>(p, causal, varlen, mode, grid, stream);
   return launch_bwd_d<64>(p, causal, varlen, mode, grid, stream);
 }
@@ -834,7 +878,10 @@ hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, flo
                           float* lse2, float* dq_acc, int* sem, long sem_count, uint32_t* hdr,
                           int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream) {
   const int grid = max(1, (rows + 15) / 16);
-  if (d == 128)
+  if (d == 256)
+    hipLaunchKernelGGL(bwd_pre_kernel<256>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
+                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
+  else if (d == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
                        lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
   else

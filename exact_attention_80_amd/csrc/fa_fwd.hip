@@ -109,9 +109,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   constexpr int BR = NW * 32;
   constexpr int CH = D / 8;                      // 16-byte chunks per key row
   using KT = PadTile<kBC, CH, CH + 1>;           // K: 16-byte operand reads
-  using VT = SwzTile<kBC, CH, D == 128 ? 20 : 12>;  // V: 8-byte transposed reads
+  // V: 8-byte transposed reads; row pitch 16 (mod 64) dwords where it fits
+  using VT = SwzTile<kBC, CH, D == 256 ? 36 : (D == 128 ? 20 : 12)>;
 
-  constexpr int STAGES = kFwdStages;             // K/V tiles in flight or in use
+  constexpr int STAGES = fwd_stages(D);          // K/V tiles in flight or in use
   __shared__ __attribute__((aligned(16))) char kv_s[STAGES][KT::kBytes + VT::kBytes];
 
   WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   // ---- direct global->LDS copy of one K and one V tile.  Rows past the
   // sequence end arrive as zeros (buffer range check); their scores are
   // masked.  Every wave issues the same number of copies per tile (kCopies).
-  constexpr int VST = D == 128 ? 20 : 12;
+  constexpr int VST = D == 256 ? 36 : (D == 128 ? 20 : 12);
   constexpr int kCopies = dma_count<KT, NW>() + dma_count<VT, NW>();
   const long kv_bytes = kv_row * 2;
   TileCopy<KT, NW> kcopy;
@@ -387,17 +388,20 @@ hipError_t launch_fwd_t(const FwdParams& p, int grid, hipStream_t stream) {
 
 }  // namespace
 
-int fwd_tile_rows() { return kFwdWaves * 32; }
+int fwd_tile_rows(int d) { return fwd_waves(d) * 32; }
 
 hipError_t launch_fwd_combine(const FwdParams& p, int d, int nseq, hipStream_t stream) {
   const long grid = (long)nseq * p.Hq;
   if (grid <= 0) return hipSuccess;
-  if (d == 128)
+  if (d == 256)
+    hipLaunchKernelGGL(fwd_combine_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+                       fwd_tile_rows(256));
+  else if (d == 128)
     hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p,
-                       kFwdWaves * 32);
+                       fwd_tile_rows(128));
   else
     hipLaunchKernelGGL(fwd_combine_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, p,
-                       kFwdWaves * 32);
+                       fwd_tile_rows(64));
   return hipGetLastError();
 }
 int fwd_tile_keys() { return kBC; }
@@ -405,6 +409,13 @@ int fwd_tile_keys() { return kBC; }
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,
                       hipStream_t stream) {
   constexpr int NW = kFwdWaves;
+  if (d == 256) {
+    constexpr int NW4 = fwd_waves(256);
+    if (causal) return varlen ? launch_fwd_t<256, NW4, true, true>(p, grid, stream)
+                              : launch_fwd_t<256, NW4, true, false>(p, grid, stream);
+    return varlen ? launch_fwd_t<256, NW4, false, true>(p, grid, stream)
+                  : launch_fwd_t<256, NW4, false, false>(p, grid, stream);
+  }
   if (d == 128) {
     if (causal) return varlen ? launch_fwd_t<128, NW, true, true>(p, grid, stream)
                               : launch_fwd_t<128, NW, true, false>(p, grid, stream);

@@ -9,9 +9,17 @@ namespace fa {
 
 constexpr int kFwdWaves = 8;   // forward workgroup: 8 waves, 256 query rows
 constexpr int kFwdStages = 4;  // forward K/V copy ring depth (tiles)
+// d = 256: 4 waves (128 query rows, one wave per SIMD with the whole register
+// file) and a 2-deep ring of 70 KB K/V tiles
+__host__ __device__ constexpr int fwd_waves(int d) { return d == 256 ? 4 : kFwdWaves; }
+__host__ __device__ constexpr int fwd_stages(int d) { return d == 256 ? 2 : kFwdStages; }
 constexpr int kBwdWaves = 8;   // backward workgroup: 8 waves, 256 keys
 constexpr int kBwdBQ = 32;     // backward query tile
 constexpr int kBwdBC = kBwdWaves * 32;
+// d = 256: 4 waves of 32 keys (128 keys, one wave per SIMD with the whole
+// register file for its dK, dV accumulators and V rows)
+__host__ __device__ constexpr int bwd_waves(int d) { return d == 256 ? 4 : kBwdWaves; }
+__host__ __device__ constexpr int bwd_tile_keys(int d) { return bwd_waves(d) * 32; }
 
 // dQ reduction across key tiles
 constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
@@ -32,7 +40,7 @@ __host__ __device__ __forceinline__ long pair_index(int i, int j, int nkv) {
   return (long)i * nkv + j;
 }
 
-int fwd_tile_rows();
+int fwd_tile_rows(int d);
 int fwd_tile_keys();
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,

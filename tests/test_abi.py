@@ -81,7 +81,7 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, N=128, Hq=2, Hkv=2, d=64, scale=0.1
     (dict(o=MIS), INVALID), (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(N=-3), INVALID),
     (dict(Hq=3, Hkv=2), INVALID), (dict(Hkv=0), INVALID), (dict(causal=2), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
-    (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=512), UNSUPPORTED),
 ])
 def test_fwd_rejects_bad_arguments(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -101,6 +101,14 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, det=-1) == INVALID
     assert bwd(lib, dq=None) == INVALID
     assert bwd(lib, d=80) == UNSUPPORTED
+    assert bwd(lib, d=512) == UNSUPPORTED
+    # d = 256 takes the atomic and ordered modes only
+    assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 0) > 0
+    assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 1) > 0
+    assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 2) == 0
+    assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 3) == 0
+    ws2 = lib.fa_bwd_workspace_size(1, 128, 2, 2, 128, 0, 2)
+    assert lib.fa_bwd(P, P, P, P, P, P, P, P, P, 1, 128, 2, 2, 256, 0.1, 0, 2, P, ws2, None) == UNSUPPORTED
     assert bwd(lib, ws=MIS) == INVALID
 
 

@@ -71,6 +71,36 @@ def test_dense_parity(fa, shape, causal):
     check_against_oracle(x, outs, causal, d)
 
 
+HEAD256_CASES = [
+    # d = 256: 4-wave workgroups (128 query rows / 128 keys); ragged tails,
+    # GQA/MQA, a single token
+    (1, 300, 2, 1, 256),
+    (2, 129, 4, 4, 256),
+    (1, 1, 2, 2, 256),
+    (1, 513, 4, 2, 256),
+]
+
+
+@pytest.mark.parametrize("det", [0, 1], ids=["atomic", "ordered"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", HEAD256_CASES, ids=lambda s: "x".join(map(str, s)))
+def test_head_dim_256_parity(fa, shape, causal, det):
+    B, N, Hq, Hkv, d = shape
+    x, _, outs = run_dense(fa, B, N, Hq, Hkv, d, causal, seed=11, deterministic=det)
+    check_against_oracle(x, outs, causal, d)
+
+
+def test_head_dim_256_ordered_is_bit_identical(fa):
+    import torch
+    x, t, outs = run_dense(fa, 1, 400, 4, 2, 256, True, seed=12, deterministic=1)
+    ref = [a.clone() for a in outs[2:]]
+    for rep in range(10):
+        g = fa.bwd(t["q"], t["k"], t["v"], outs[0], outs[1], t["do"], causal=True,
+                   softmax_scale=scale_for(256), deterministic=1)
+        for a, b in zip(g, ref):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rep
+
+
 @pytest.mark.parametrize("mode", [1, 2, 3], ids=["ordered", "partial", "fused"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_dense_parity_deterministic(fa, causal, mode):

@@ -196,6 +196,20 @@ def test_mha_2k(fa, d, causal):
     check_dv_sum(grads[2], prob.t["do"], 1)
 
 
+# ---- head dimension 256: B=2 H=8 N=4096 causal -------------------------------------
+
+@pytest.mark.parametrize("det", [0, 1], ids=["atomic", "ordered"])
+def test_head_dim_256_whole_head(fa, det):
+    prob = dense_problem(fa, 2, 4096, 8, 8, 256, True, seed=4)
+    grads = prob.backward(det)
+    say("oracle head b=1 h=7 (d=256)")
+    ref = ora.head_forward_backward(*prob.head(1, 7), prob.scale, True)
+    check_whole_head(prob, grads, 1, 7, ref)
+    check_rows(prob, grads, 0, 0, seed=1)
+    check_last_keys(prob, grads, 0, 3)
+    check_dv_sum(grads[2], prob.t["do"], 1)
+
+
 # ---- long context B=1 H=16 N=16384/32768 ----------------------------------------
 
 @pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])

@@ -52,6 +52,7 @@ QK_CASES = [
     ([300, 64, 5, 40], [100, 64, 1, 700], 2, 2, 64),           # more queries than keys
     ([0, 7, 129, 1], [50, 0, 513, 257], 4, 1, 128),            # empty sequences
     ([256, 257, 31], [1000, 600, 31], 4, 4, 64),               # chunked prefill
+    ([1, 130, 40, 0], [300, 129, 20, 17], 2, 1, 256),          # d = 256
 ]
 
 
@@ -84,6 +85,7 @@ SPLIT_CASES = [
     # into chunks of 32 key tiles and merged by the combine kernel
     ([1, 17, 32, 33, 257, 288, 289], [5000, 5000, 2049, 5000, 3000, 2100, 2100], 4, 2, 128),
     ([1, 3], [70000, 4100], 2, 1, 64),
+    ([1, 129, 160], [4500, 3000, 2100], 2, 2, 256),
 ]
 
 
