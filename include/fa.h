@@ -32,7 +32,8 @@
  *    nseq+1 entries; it is validated on the device (first 0, last T,
  *    non-decreasing) and a violation is reported through the workspace error
  *    word (fa_workspace_error), not by the return value.
- *  - d (head dimension) is 64 or 128.  Hq must be a positive multiple of Hkv;
+ *  - d (head dimension) is 64, 128 or 256 (256: the fa_bwd partial-tile modes
+ *    deterministic == 2, 3 are not offered).  Hq must be a positive multiple of Hkv;
  *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
  *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2)
  *    when queries and keys have the same length.  The fa_varlen_qk_* calls
@@ -67,7 +68,7 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,    /* null pointer, bad size, misalignment, bad flag */
-  FA_ERR_UNSUPPORTED = 2,    /* valid but not implemented (e.g. d not in {64,128}) */
+  FA_ERR_UNSUPPORTED = 2,    /* valid but not implemented (e.g. d not in {64,128,256}) */
   FA_ERR_WORKSPACE = 3,      /* workspace missing or smaller than required */
   FA_ERR_HIP = 4,            /* a HIP runtime call or kernel launch failed */
   FA_ERR_DEVICE = 5,         /* current device is not a gfx950 GPU */
