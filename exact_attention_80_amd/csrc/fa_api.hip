@@ -240,6 +240,7 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, long Tk, int H
     } else {
       l.sem_count = (long)B * Hq * cdiv(N, fa::kBwdBQ);
     }
+    l.sem_count *= fa::bwd_col_halves(d);  // one per column half of a dQ tile
   }
   l.sem = off;
   off += align_up((size_t)l.sem_count * 4);
@@ -431,6 +432,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     p.nq = (int)cdiv(N, fa::kBwdBQ);
     grid = (long)B * Hkv * lay.S * p.nkv;
   }
+  grid *= fa::bwd_col_halves(d);  // d = 256: one workgroup per column half
   if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   if (grid > 0) {
     tk = timing_start(1, s);

@@ -86,6 +86,11 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   constexpr int NW = bwd_waves(D);  // waves of 32 keys (shadows the d <= 128 defaults)
   constexpr int NT = NW * 64;
   constexpr int BC = NW * 32;
+  // d = 256: each workgroup owns one half of the head dimension for dK, dV
+  // and dQ (S and dP still use all of it), so its accumulators fit the
+  // register file; two workgroups share a key tile
+  constexpr int NHALF = bwd_col_halves(D);
+  constexpr int DH = D / NHALF;     // output columns per workgroup
   constexpr bool DET = DQM == kDqOrdered;
   constexpr bool FUSED = DQM == kDqFused;
   constexpr bool PARTS = DQM == kDqPartial || FUSED;  // partial tiles in dq_part
@@ -123,6 +128,9 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   } else {
     r = blockIdx.x;
   }
+  const int chalf = NHALF > 1 ? (r % NHALF) : 0;  // output column half
+  r /= NHALF;
+  const int dh0 = chalf * DH;                     // first output column
   BwdItem it;
   const int HS = p.Hkv * p.S;
   if (VARLEN) {
@@ -197,9 +205,9 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   }
   wait_vmem();  // V rows and the K tile are in before the loop starts
 
-  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+  f32x16 dk_acc[DH / 32], dv_acc[DH / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) { dk_acc[db][x] = 0.f; dv_acc[db][x] = 0.f; }
 
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   // d = 64: one of each; d = 256: four column blocks, both row blocks), over
   // all BC keys, so no partial sums are exchanged and every wave adds its own
   // blocks.
-  constexpr int DB16 = D / 16;               // 16-column blocks of dQ
+  constexpr int DB16 = DH / 16;              // 16-column blocks of dQ (this workgroup's)
   constexpr int UPW = (2 * DB16) / NW;       // (row block, column block) units per wave
   constexpr int NQB = UPW >= 2 ? 2 : 1;      // 16-row blocks per wave
   constexpr int NCB = UPW / NQB;             // 16-column blocks per wave
@@ -274,8 +282,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   int k_tr[NCB][2];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
-    k_tr[c][0] = KT::off(rk, 16 * (dblk + c) + 4 * (L16 & 3));
-    k_tr[c][1] = KT::off(rk + 4, 16 * (dblk + c) + 4 * (L16 & 3));
+    k_tr[c][0] = KT::off(rk, dh0 + 16 * (dblk + c) + 4 * (L16 & 3));
+    k_tr[c][1] = KT::off(rk + 4, dh0 + 16 * (dblk + c) + 4 * (L16 & 3));
   }
   int ds_tr[NQB][2];
 #pragma unroll
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
       // byte offset of this lane's element in row 16 qb0 + 4 g16 of the tile;
       // rebuilt per item (the empty asm keeps the compiler from holding 4 NQB
       // offsets in registers across the whole loop)
-      int vo = ((16 * qb0 + 4 * g16) * (int)q_row + dblk * 16 + L16) * 4;
+      int vo = ((16 * qb0 + 4 * g16) * (int)q_row + dh0 + dblk * 16 + L16) * 4;
       asm volatile("" : "+v"(vo));
       const int row_bytes = (int)q_row * 4;
 #pragma unroll
@@ -378,13 +386,14 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
             (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
                 acc[c * NQB + qb][r], rsrc, vo + (16 * qb + r) * row_bytes + 64 * c, 0, 0);
     } else {
-      float* dq_base = p.dq_acc + (long)it.q_start * q_row + (long)h * D + dblk * 16 + L16;
+      float* dq_base = p.dq_acc + (long)it.q_start * q_row + (long)h * D + dh0 + dblk * 16 + L16;
       // ordered reduction: writers of a dQ tile apply in descending key-tile order
       const int jhi = CAUSAL ? min(it.nkv - 1, (q0 + BQ - 1 + it.off) / BC) : it.nkv - 1;
       const int rank = jhi - it.jt;
       long sidx;
       if (VARLEN) sidx = (long)h * p.sem_slots + it.q_start / BQ + it.seq + i;
       else sidx = ((long)it.seq * p.Hq + h) * p.nq + i;
+      sidx = sidx * NHALF + chalf;  // each column half has its own order
       int* semp = p.sem + sidx;
       // Wait for our turn.  The semaphore and the dQ accumulator are only ever
       // touched by device-scope atomics, which are performed at the coherence
@@ -488,9 +497,9 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 64 * db;
-          const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 64 * db;
+        for (int db = 0; db < DH / 32; ++db) {
+          const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
+          const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
           const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
           const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
           dv_acc[db] = mfma32x32x16(pa[qc], bdo, dv_acc[db]);
@@ -631,14 +640,15 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   }
 
   // ---------------- dK = scale * sum dS^T Q, dV = sum P^T dO for this wave's keys
-  // dk_acc[db][x] = dK[key = wk0 + 8(x/4) + 4 half + x%4][d = 32 db + l32]
+  // dk_acc[db][x] = dK[key = wk0 + 8(x/4) + 4 half + x%4][d = dh0 + 32 db + l32]
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int key = wk0 + 8 * (x >> 2) + 4 * half + (x & 3);
       if (key < it.k_len) {
-        const long off = ((long)it.k_start + key) * kv_row + (long)it.hkv * D + db * 32 + l32;
+        const long off =
+            ((long)it.k_start + key) * kv_row + (long)it.hkv * D + dh0 + db * 32 + l32;
         if (p.S == 1) {
           p.dk[off] = (bf16)(dk_acc[db][x] * p.scale);
           p.dv[off] = (bf16)(dv_acc[db][x]);

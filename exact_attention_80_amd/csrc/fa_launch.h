@@ -20,6 +20,9 @@ constexpr int kBwdBC = kBwdWaves * 32;
 // register file for its dK, dV accumulators and V rows)
 __host__ __device__ constexpr int bwd_waves(int d) { return d == 256 ? 4 : kBwdWaves; }
 __host__ __device__ constexpr int bwd_tile_keys(int d) { return bwd_waves(d) * 32; }
+// d = 256: two workgroups per key tile, one per half of the dK / dV / dQ
+// columns (both recompute S and dP over the whole head dimension)
+__host__ __device__ constexpr int bwd_col_halves(int d) { return d == 256 ? 2 : 1; }
 
 // dQ reduction across key tiles
 constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
