@@ -4,7 +4,9 @@
 //  * preprocess: D = rowsum(dO o O) per query row (fp32), and the fp32 dQ
 //    accumulator, the ordering semaphores and the workspace header are zeroed;
 //  * main kernel: one workgroup per (sequence, key/value head, key tile of 256
-//    keys, query-head subgroup).  Each of the 8 waves owns 32 keys and keeps its
+//    keys -- 128 for d = 256, with one workgroup per half of the output
+//    columns --, query-head subgroup).  Each of the 8 (d = 256: 4) waves owns
+//    32 keys and keeps its
 //    K and V rows and its dK, dV accumulators in registers for the whole
 //    kernel.  The workgroup walks every query head of its key/value head
 //    (subgroup) and, per head, the 32-row query tiles from the diagonal

@@ -2,12 +2,14 @@
 //
 // Method ([FA2] "Core method" 1-3, [FA4N] co-design list):
 //  * one workgroup per (sequence, query head, query tile of BR = 32*NW rows);
-//    the tiles are independent, so the output never depends on launch order;
+//    the tiles are independent, so the output never depends on launch order
+//    (a split tile's key chunks are merged in a fixed order afterwards);
 //  * split-Q: wave w owns query rows 32w..32w+31 of the tile and sees every
 //    key/value tile, so no reduction between waves is ever needed;
 //  * K and V tiles of 64 keys are copied global->LDS by direct loads (no
-//    register staging) into padded tiles, through a ring of kFwdStages
-//    buffers: the next tiles are in flight while tile j is computed;
+//    register staging) into padded tiles, through a ring of fwd_stages(D)
+//    buffers (4; 2 for d = 256, whose workgroups have 4 waves): the next
+//    tiles are in flight while tile j is computed;
 //  * the score tile is computed transposed, S^T = K Q^T, so each lane holds one
 //    query column: the row max and row sum are in-lane plus one exchange
 //    between lane halves;

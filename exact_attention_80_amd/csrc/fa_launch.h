@@ -7,13 +7,13 @@
 
 namespace fa {
 
-constexpr int kFwdWaves = 8;   // forward workgroup: 8 waves, 256 query rows
+constexpr int kFwdWaves = 8;   // forward workgroup (d <= 128): 8 waves, 256 query rows
 constexpr int kFwdStages = 4;  // forward K/V copy ring depth (tiles)
 // d = 256: 4 waves (128 query rows, one wave per SIMD with the whole register
 // file) and a 2-deep ring of 70 KB K/V tiles
 __host__ __device__ constexpr int fwd_waves(int d) { return d == 256 ? 4 : kFwdWaves; }
 __host__ __device__ constexpr int fwd_stages(int d) { return d == 256 ? 2 : kFwdStages; }
-constexpr int kBwdWaves = 8;   // backward workgroup: 8 waves, 256 keys
+constexpr int kBwdWaves = 8;   // backward workgroup (d <= 128): 8 waves, 256 keys
 constexpr int kBwdBQ = 32;     // backward query tile
 constexpr int kBwdBC = kBwdWaves * 32;
 // d = 256: 4 waves of 32 keys (128 keys, one wave per SIMD with the whole
