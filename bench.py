@@ -310,7 +310,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+              "sharding across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
