@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
+MFMA_FP8_PEAK_TFLOPS = 5033.2  # MI355X dense fp8 (twice the bf16 rate)
 METRIC = "attention fwd+bwd TFLOPs/s (bf16, d=128, causal N=8K) and % of MFMA peak"
 
 
@@ -405,6 +406,25 @@ def main():
             extras[f"bwd_mode{mode}_post_ms"] = kd["bwd_post"][1] / args.steps
             extras[f"bwd_mode{mode}_tflops"] = f_bwd / (mode_ms * 1e-3) / 1e12
             extras[f"bwd_mode{mode}_over_this"] = this_ms / mode_ms
+        if d in (64, 128) and args.steps > 0:
+            # the forward with fp8 (e4m3) Q and K for the scores, per-tensor descale factors
+            qd = float(x["q"].float().abs().max()) / 448.0
+            kd = float(x["k"].float().abs().max()) / 448.0
+            q8 = (x["q"].float() / qd).to(torch.float8_e4m3fn)
+            k8 = (x["k"].float() / kd).to(torch.float8_e4m3fn)
+            for _ in range(3):
+                fa.fwd_fp8(q8, k8, x["v"], qd, kd, causal=causal, softmax_scale=scale)
+            torch.cuda.synchronize()
+            fa.timing_begin()
+            for _ in range(args.steps):
+                fa.fwd_fp8(q8, k8, x["v"], qd, kd, causal=causal, softmax_scale=scale)
+            kf = fa.timing_end()["fwd"]
+            fp8_ms = kf[1] / max(1, kf[0])
+            extras["fp8_fwd_kernel_ms"] = fp8_ms
+            extras["fp8_fwd_tflops"] = f_fwd / (fp8_ms * 1e-3) / 1e12
+            extras["fp8_fwd_pct_fp8_peak"] = 100.0 * extras["fp8_fwd_tflops"] / MFMA_FP8_PEAK_TFLOPS
+            extras["fp8_fwd_speedup_vs_bf16"] = avg_fwd_ms / fp8_ms
+            del q8, k8
 
     metric = METRIC
     if (B, N, Hq, Hkv, d, causal) != (2, 8192, 16, 16, 128, True):

@@ -500,6 +500,51 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                  Hkv, d, softmax_scale, causal, ws, ws_bytes, stream);
 }
 
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse, int B, int N,
+               int Hq, int Hkv, int d, float softmax_scale, float q_descale, float k_descale,
+               int causal, void* stream) {
+  if (!dense_ok(B, N)) return fail(FA_ERR_INVALID_ARG, "B and N must be positive");
+  int st;
+  if ((st = check_ptr(q8, "q8")) || (st = check_ptr(k8, "k8")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
+    return st;
+  if ((st = check_dims((long)B * N, Hq, Hkv, d, causal, softmax_scale))) return st;
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fp8 scores support head dimension 64 or 128");
+  if (!(q_descale > 0.f) || !std::isfinite(q_descale) || !(k_descale > 0.f) ||
+      !std::isfinite(k_descale))
+    return fail(FA_ERR_INVALID_ARG, "descale factors must be positive and finite");
+  const float c = softmax_scale * q_descale * k_descale * fa::kLog2e;
+  if (!std::isfinite(c) || !(c > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "softmax_scale * q_descale * k_descale out of range");
+  std::string why;
+  if ((st = check_device(&why))) return fail(st, why);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FwdParams p{};
+  p.q8 = static_cast<const uint8_t*>(q8);
+  p.k8 = static_cast<const uint8_t*>(k8);
+  p.v = static_cast<const fa::bf16*>(v);
+  p.o = static_cast<fa::bf16*>(o);
+  p.lse = lse;
+  p.B = B;
+  p.N = N;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.T = (int)((long)B * N);
+  p.sched = sched_mode();
+  p.c = c;
+  p.nq = (int)cdiv(N, fa::fwd_tile_rows(d));
+  const long grid = (long)p.nq * B * Hq;
+  if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const long tk = timing_start(0, s);
+  const hipError_t e = fa::launch_fwd_fp8(p, d, causal != 0, (int)grid, s);
+  timing_stop(tk, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
+  return FA_OK;
+}
+
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;

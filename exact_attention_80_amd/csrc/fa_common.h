@@ -50,6 +50,16 @@ __host__ __device__ __forceinline__ int fwd_split_chunk_tiles(int nt) {
   return c > 32 ? c : 32;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 product of fp8 (OCP e4m3) operands, fp32 accumulate.  Lane l
+// supplies row l % 32 of A (column l % 32 of B) for 32 of the 64 reduction
+// indices; A and B pair their bytes position by position, so any assignment
+// of the reduction indices to (lane half, byte) works if both use it.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -400,6 +410,8 @@ struct FwdParams {
   const bf16* v;
   bf16* o;
   float* lse;
+  const uint8_t* q8;      // fp8 scores: Q and K as OCP e4m3 bytes (c then includes
+  const uint8_t* k8;      // their descale factors)
   const int* cu_seqlens;  // varlen only: query offsets
   const int* cu_seqlens_k;  // varlen only: key offsets (the same array when Lq == Lk)
   const int* tiles;       // varlen only: (sequence, q-tile) pairs in schedule order

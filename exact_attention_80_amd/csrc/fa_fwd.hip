@@ -106,11 +106,13 @@ __device__ __forceinline__ WorkItem fwd_work_item(const FwdParams& p) {
   return w;
 }
 
-template <int D, int NW, bool CAUSAL, bool VARLEN>
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool FP8 = false>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   constexpr int BR = NW * 32;
-  constexpr int CH = D / 8;                      // 16-byte chunks per key row
-  using KT = PadTile<kBC, CH, CH + 1>;           // K: 16-byte operand reads
+  constexpr int EB = FP8 ? 1 : 2;                // bytes per Q / K element
+  constexpr int CH = D / 8;                      // 16-byte chunks per bf16 row (V)
+  constexpr int KCH = D * EB / 16;               // 16-byte chunks per K row
+  using KT = PadTile<kBC, KCH, KCH + 1>;         // K: 16-byte operand reads
   // V: 8-byte transposed reads; row pitch 16 (mod 64) dwords where it fits
   using VT = SwzTile<kBC, CH, D == 256 ? 36 : (D == 128 ? 20 : 12)>;
 
@@ -134,8 +136,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int hkv = wi.h / p.G;
   const long q_row = (long)p.Hq * D;   // elements between consecutive tokens
   const long kv_row = (long)p.Hkv * D;
-  const bf16* qbase = p.q + (long)wi.seq_start * q_row + (long)wi.h * D;
-  const bf16* kbase = p.k + (long)wi.k_start * kv_row + (long)hkv * D;
+  const char* qbase = reinterpret_cast<const char*>(FP8 ? (const void*)p.q8 : (const void*)p.q) +
+                      ((long)wi.seq_start * q_row + (long)wi.h * D) * EB;
+  const char* kbase = reinterpret_cast<const char*>(FP8 ? (const void*)p.k8 : (const void*)p.k) +
+                      ((long)wi.k_start * kv_row + (long)hkv * D) * EB;
   const bf16* vbase = p.v + (long)wi.k_start * kv_row + (long)hkv * D;
   const int klen = wi.k_len;
   const int off = wi.off;
@@ -144,12 +148,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int wq0 = q0 + wave * 32;
   const int qi = wq0 + l32;
   const bool q_ok = qi < wi.seq_len;
-  bf16x8 qf[D / 16];
+  // bf16: 8 values per lane per 16-wide step; fp8: 32 bytes per lane per
+  // 64-wide step (head-dim elements 64t + 32 half .. +31)
+  constexpr int NQF = FP8 ? D / 64 : D / 16;
+  bf16x8 qf[FP8 ? 1 : D / 16];
+  i32x8 qf8[FP8 ? D / 64 : 1];
 #pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (q_ok) u = ld_global16(qbase + (long)qi * q_row + dc * 16 + half * 8);
-    qf[dc] = as_bf16x8(u);
+  for (int dc = 0; dc < NQF; ++dc) {
+    if (FP8) {
+      u32x4 u0 = {0u, 0u, 0u, 0u}, u1 = {0u, 0u, 0u, 0u};
+      if (q_ok) {
+        const char* src = qbase + (long)qi * q_row + 64 * dc + 32 * half;
+        u0 = ld_global16(src);
+        u1 = ld_global16(src + 16);
+      }
+      qf8[dc] = i32x8{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                      (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+    } else {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (q_ok) u = ld_global16(qbase + ((long)qi * q_row + dc * 16 + half * 8) * 2);
+      qf[dc] = as_bf16x8(u);
+    }
   }
 
   const int kv_end = CAUSAL ? max(0, min(klen, q0 + BR + off)) : klen;
@@ -165,17 +184,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   // masked.  Every wave issues the same number of copies per tile (kCopies).
   constexpr int VST = D == 256 ? 36 : (D == 128 ? 20 : 12);
   constexpr int kCopies = dma_count<KT, NW>() + dma_count<VT, NW>();
-  const long kv_bytes = kv_row * 2;
+  const long kv_bytes = kv_row * 2;     // V row pitch (bf16)
+  const long k_bytes = kv_row * EB;     // K row pitch
   TileCopy<KT, NW> kcopy;
   TileCopy<VT, NW> vcopy;
-  kcopy.init(kv_bytes, CH + 1, wave, lane, [](int, int pc) { return pc < CH ? pc : -1; });
+  kcopy.init(k_bytes, KCH + 1, wave, lane, [](int, int pc) { return pc < KCH ? pc : -1; });
   vcopy.init(kv_bytes, VST, wave, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
   auto issue_tile = [&](int u) {  // the u-th tile of this item, key tile jb + u
     char* kt = kv_s[u % STAGES];
     const int j = jb + u;
-    const uint32_t range = tile_range(j * kBC, klen, kv_bytes, D * 2);
-    kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * kv_row, range));
-    vcopy.issue(kt + KT::kBytes, make_rsrc(vbase + (long)j * kBC * kv_row, range));
+    kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * k_bytes,
+                              tile_range(j * kBC, klen, k_bytes, D * EB)));
+    vcopy.issue(kt + KT::kBytes, make_rsrc(vbase + (long)j * kBC * kv_row,
+                                           tile_range(j * kBC, klen, kv_bytes, D * 2)));
   };
 
   // ---- running softmax state (per lane = per query; both lane halves agree)
@@ -200,12 +221,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    if (FP8) {
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
+      for (int dc = 0; dc < D / 64; ++dc) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = as_bf16x8(ld_lds16(kt + KT::off(kb * 32 + l32, 16 * dc + 8 * half)));
-        s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const char* src = kt + (kb * 32 + l32) * KT::kPitch + 64 * dc + 32 * half;
+          const u32x4 a0 = ld_lds16(src), a1 = ld_lds16(src + 16);
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          s[kb] = mfma32x32x64_fp8(a, qf8[dc], s[kb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = as_bf16x8(ld_lds16(kt + KT::off(kb * 32 + l32, 16 * dc + 8 * half)));
+          s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
+        }
       }
     }
     const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0 + off) || (key0 + kBC > klen);
@@ -382,15 +417,25 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p, int br) {
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool VARLEN>
+template <int D, int NW, bool CAUSAL, bool VARLEN, bool FP8 = false>
 hipError_t launch_fwd_t(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VARLEN>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, CAUSAL, VARLEN, FP8>), dim3(grid), dim3(NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int fwd_tile_rows(int d) { return fwd_waves(d) * 32; }
+
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, int grid, hipStream_t stream) {
+  constexpr int NW = kFwdWaves;
+  if (d == 128)
+    return causal ? launch_fwd_t<128, NW, true, false, true>(p, grid, stream)
+                  : launch_fwd_t<128, NW, false, false, true>(p, grid, stream);
+  return causal ? launch_fwd_t<64, NW, true, false, true>(p, grid, stream)
+                : launch_fwd_t<64, NW, false, false, true>(p, grid, stream);
+}
 
 hipError_t launch_fwd_combine(const FwdParams& p, int d, int nseq, hipStream_t stream) {
   const long grid = (long)nseq * p.Hq;

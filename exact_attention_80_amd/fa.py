@@ -33,6 +33,7 @@ _SIGS = {
     "fa_last_error": ([], ctypes.c_char_p),
     "fa_fwd_workspace_size": ([_i] * 6, _sz),
     "fa_fwd": ([_p] * 5 + [_i] * 5 + [_f, _i, _p, _sz, _p], _i),
+    "fa_fwd_fp8": ([_p] * 5 + [_i] * 5 + [_f, _f, _f, _i, _p], _i),
     "fa_bwd_workspace_size": ([_i] * 7, _sz),
     "fa_bwd": ([_p] * 9 + [_i] * 5 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_varlen_fwd_workspace_size": ([_i] * 6, _sz),
@@ -111,6 +112,33 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None):
     _check(_lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
                        _ptr(ws), ws_n, _stream()), "fa_fwd")
+    return o, lse
+
+
+def _e4m3_bytes(t, name, shape):
+    """fp8 operands travel as their raw e4m3 bytes (uint8 or float8_e4m3fn tensors)."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _need(t, name, shape, torch.uint8)
+    return t
+
+
+def fwd_fp8(q8, k8, v, q_descale: float, k_descale: float, causal: bool = False,
+            softmax_scale: float | None = None):
+    """Dense forward with fp8 scores: q8 [B,N,Hq,d], k8 [B,N,Hkv,d] OCP e4m3 bytes
+    (uint8 or float8_e4m3fn) standing for q_descale * q8 and k_descale * k8, v
+    [B,N,Hkv,d] bf16 -> (o [B,N,Hq,d] bf16, lse [B,Hq,N] fp32).  d = 64 or 128."""
+    B, N, Hq, d = q8.shape
+    Hkv = k8.shape[2]
+    q8 = _e4m3_bytes(q8, "q8", (B, N, Hq, d))
+    k8 = _e4m3_bytes(k8, "k8", (B, N, Hkv, d))
+    _need(v, "v", (B, N, Hkv, d))
+    o = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=v.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=v.device)
+    _check(_lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), B, N, Hq, Hkv, d, _scale(d, softmax_scale),
+                           float(q_descale), float(k_descale), int(causal), _stream()),
+           "fa_fwd_fp8")
     return o, lse
 
 

@@ -21,6 +21,11 @@ Recipe:
     query count is an integer drawn uniformly from [1, min(Lk, qmax)] (a
     chunk of new tokens); Q, dO are [Tq, Hq, d] and K, V [Tk, Hkv, d], drawn
     in the order Q, K, V, dO.
+  * fp8 scores: the dense draws above before bf16 rounding; Q and K are each
+    quantised per tensor to OCP e4m3 ("fn": largest finite 448, no
+    infinities) with descale = amax(|x|) / 448 in float32 and bytes
+    e4m3(x / descale), rounded to nearest, ties to even; V is bf16-rounded.
+    The attention inputs the bytes stand for are descale * e4m3 value.
 """
 
 from __future__ import annotations
@@ -127,3 +132,71 @@ def varlen_qk_inputs(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, seed: int 
     out["cu_seqlens_q"] = cu_seqlens(lengths_q)
     out["cu_seqlens_k"] = cu_seqlens(lengths_k)
     return out
+
+
+# ---------------------------------------------------------------------------
+# OCP 8-bit floating point, e4m3 "fn" variant: 1 sign bit, 4 exponent bits
+# (bias 7), 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6;
+# the all-ones pattern 0x7f / 0xff is NaN, so the largest finite value is
+# 0x7e = 1.75 * 2^8 = 448 and there are no infinities.
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Magnitudes of codes 0..127 (code 127, NaN in the format, gets 480: the
+    value its bits would have, used only as the rounding neighbour of 448)."""
+    c = np.arange(128)
+    e = c >> 3
+    m = (c & 7).astype(np.float64)
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+
+
+_E4M3_MAG = _e4m3_magnitudes()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of e4m3 bytes (uint8); NaN codes give NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    v = _E4M3_MAG[c & 0x7F]
+    v = np.where(c & 0x80, -v, v)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round values to the nearest e4m3 byte, ties to the even code; a value
+    that would round beyond 448 raises ValueError (the format has no
+    infinities).  Returns uint8."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("e4m3_encode takes finite values only")
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(_E4M3_MAG, a, side="left"), 1, 127)
+    lo = hi - 1
+    dlo = a - _E4M3_MAG[lo]
+    dhi = _E4M3_MAG[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    if np.any(code == 127) or np.any(a > _E4M3_MAG[127]):
+        raise ValueError("value out of the e4m3 range (largest finite 448)")
+    sign = np.signbit(x)  # values that round to zero keep their sign (-0 is 0x80)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3(x) -> tuple[np.ndarray, float]:
+    """Per-tensor e4m3 quantisation: (bytes, descale) with descale =
+    float32(amax / 448) so that descale * e4m3_decode(bytes) approximates x."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    return e4m3_encode(x.astype(np.float64) / descale), descale
+
+
+def fp8_dense_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, seed: int = 0) -> dict:
+    """Dense fp8-score inputs: q8, k8 (uint8 e4m3 bytes), their descale
+    factors, V (bf16-rounded float32) and the attention inputs q, k the bytes
+    stand for (float64: descale * decoded value)."""
+    raw = dense_inputs(B, N, Hq, Hkv, d, seed, round_bf16=False)
+    q8, qd = quantize_e4m3(raw["q"])
+    k8, kd = quantize_e4m3(raw["k"])
+    return {"q8": q8, "k8": k8, "q_descale": qd, "k_descale": kd,
+            "q": qd * e4m3_decode(q8), "k": kd * e4m3_decode(k8),
+            "v": bf16_round(raw["v"])}

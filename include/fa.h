@@ -105,6 +105,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int N, int Hq, int Hkv, int d, float softmax_scale, int causal,
            void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Forward pass with fp8 scores ([FA2] "Limitations and future work": FP8
+ * specialisations of the kernel are named there as the next step):
+ *   S = scale * (q_descale * Q8) (k_descale * K8)^T,
+ *   O = softmax(S [causal mask]) V,   LSE_i = ln sum_j exp(S_ij).
+ * q8 [B,N,Hq,d] and k8 [B,N,Hkv,d] hold one byte per element in the OCP
+ * e4m3 format (the "fn" variant: no infinities, 0x7f / 0xff are NaN, largest
+ * finite 448); q_descale and k_descale (positive, finite) are the per-tensor
+ * factors that turn the stored values back into Q and K.  The product Q8 K8^T
+ * is exact in the fp32 accumulator up to the order of the additions; P is
+ * rounded to bf16 for the P V product as in fa_fwd.  v [B,N,Hkv,d] bf16, o
+ * [B,N,Hq,d] bf16, lse [B,Hq,N] fp32 as in fa_fwd.  d = 64 or 128 (anything
+ * else: FA_ERR_UNSUPPORTED); no workspace.  This call has no backward: the
+ * fp8 inputs are meant for inference.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
+               int B, int N, int Hq, int Hkv, int d, float softmax_scale,
+               float q_descale, float k_descale, int causal, void* stream);
+
 /* ---- dense backward ----------------------------------------------------- */
 
 /* Workspace bytes fa_bwd needs (D = rowsum(dO o O), the fp32 dQ accumulator or,

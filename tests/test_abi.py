@@ -23,6 +23,7 @@ def lib():
     L = ctypes.CDLL(build.LIB_PATH)
     p, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [p] * 5 + [i] * 5 + [f, i, p, sz, p]
+    L.fa_fwd_fp8.argtypes = [p] * 5 + [i] * 5 + [f, f, f, i, p]
     L.fa_bwd.argtypes = [p] * 9 + [i] * 5 + [f, i, i, p, sz, p]
     L.fa_varlen_fwd.argtypes = [p] * 6 + [i] * 6 + [f, i, p, sz, p]
     L.fa_varlen_bwd.argtypes = [p] * 10 + [i] * 6 + [f, i, i, p, sz, p]
@@ -49,12 +50,12 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_varlen_qk_fwd",
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_varlen_qk_fwd",
               "fa_varlen_qk_bwd", "fa_fwd_workspace_size",
               "fa_bwd_workspace_size", "fa_status_string", "fa_workspace_error"):
         assert n in names
@@ -85,6 +86,24 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, N=128, Hq=2, Hkv=2, d=64, scale=0.1
 ])
 def test_fwd_rejects_bad_arguments(lib, kw, status):
     assert fwd(lib, **kw) == status
+    assert lib.fa_last_error()
+
+
+def fwd_fp8(lib, q8=P, k8=P, v=P, o=P, lse=P, B=1, N=128, Hq=2, Hkv=2, d=64, scale=0.125,
+            qd=0.01, kd=0.02, causal=0):
+    return lib.fa_fwd_fp8(q8, k8, v, o, lse, B, N, Hq, Hkv, d, scale, qd, kd, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q8=None), INVALID), (dict(k8=None), INVALID), (dict(v=None), INVALID),
+    (dict(q8=MIS), INVALID), (dict(B=0), INVALID), (dict(Hq=3, Hkv=2), INVALID),
+    (dict(causal=2), INVALID), (dict(scale=0.0), INVALID), (dict(qd=0.0), INVALID),
+    (dict(kd=-1.0), INVALID), (dict(qd=float("inf")), INVALID), (dict(kd=float("nan")), INVALID),
+    (dict(qd=1e30, kd=1e30), INVALID),
+    (dict(d=256), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+])
+def test_fwd_fp8_rejects_bad_arguments(lib, kw, status):
+    assert fwd_fp8(lib, **kw) == status
     assert lib.fa_last_error()
 
 
