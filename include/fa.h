@@ -6,7 +6,8 @@
  * follows the pages describing FlashAttention-2 and FlashAttention-4:
  *   [FA2]  "FlashAttention-2: Faster Attention with Better Parallelism and Work
  *          Partitioning (ICLR 2024)" (wiki summary), sections "Problem and
- *          motivation" and "Core method" 1-4;
+ *          motivation", "Core method" 1-4 and "Limitations and future work"
+ *          (FP8 kernels);
  *   [FA4B] "FlashAttention-4 backward optimisation: 2-CTA mode and performance"
  *          (blog), sections 2.1 (global atomics for dQ), 3.2 (semaphore-ordered
  *          deterministic reduction), 3.3.1 (shortest-processing-time order for
@@ -14,12 +15,16 @@
  *          order for variable-length batches), 5.2 (walk every query head of a
  *          key/value head together), 5.3 (bf16 operands, fp32 accumulation);
  *   [FA4N] "FlashAttention-4 wird offiziell veroeffentlicht" (news article),
- *          section on the co-design ideas (conditional softmax rescaling).
+ *          section on the co-design ideas (conditional softmax rescaling);
+ *   [FA4C] "FlashAttention-4: memory and compute efficiency of GPU attention"
+ *          (codechina article), section 5.1 (an FP8 compute mode for
+ *          data-centre GPUs).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are caller-owned DEVICE memory (e.g. PyTorch allocations), dense,
- *    contiguous, 16-byte aligned.  Q, K, V, O, dO, dQ, dK, dV are bf16.
+ *    contiguous, 16-byte aligned.  Q, K, V, O, dO, dQ, dK, dV are bf16
+ *    (fa_fwd_fp8 alone takes Q and K as one-byte e4m3 values).
  *    The library never allocates or frees device memory.  Its only host state
  *    is a per-device property cache and the opt-in timing event pool below,
  *    so calls on different streams are independent as long as their buffers
@@ -33,7 +38,8 @@
  *    non-decreasing) and a violation is reported through the workspace error
  *    word (fa_workspace_error), not by the return value.
  *  - d (head dimension) is 64, 128 or 256 (256: the fa_bwd partial-tile modes
- *    deterministic == 2, 3 are not offered).  Hq must be a positive multiple of Hkv;
+ *    deterministic == 2, 3 are not offered; fa_fwd_fp8 takes 64 or 128).
+ *    Hq must be a positive multiple of Hkv;
  *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
  *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2)
  *    when queries and keys have the same length.  The fa_varlen_qk_* calls
@@ -106,8 +112,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Forward pass with fp8 scores ([FA2] "Limitations and future work": FP8
- * specialisations of the kernel are named there as the next step):
+ * Forward pass with fp8 scores ([FA2] "Limitations and future work" names
+ * FP8 kernels as the next step; [FA4C] 5.1):
  *   S = scale * (q_descale * Q8) (k_descale * K8)^T,
  *   O = softmax(S [causal mask]) V,   LSE_i = ln sum_j exp(S_ij).
  * q8 [B,N,Hq,d] and k8 [B,N,Hkv,d] hold one byte per element in the OCP
