@@ -85,3 +85,33 @@ def test_fp8_forward_wide_score_range(fa):
     err = np.abs(to_host(lse)[0] - rlse[0])
     say(f"lse err {float(err.max()):.2e}, bound from 2^-14 * max |q||k| up to {float(mag.max()) * 2.0 ** -14:.2e}")
     assert np.all(err <= TOL_LSE + 2.0 ** -14 * mag)
+
+
+def test_fp8_forward_full_size(fa):
+    """The benchmark's fp8 launch: B=2 H=16 N=8192 d=128 causal.  One whole
+    head against the oracle, and sampled query rows (the first and last 32
+    plus 96 random ones) of four more heads."""
+    import torch
+    B, N, H, d = 2, 8192, 16, 128
+    say(f"fp8 fwd full size B={B} N={N} H={H} d={d} causal")
+    x = inputs.fp8_dense_inputs(B, N, H, H, d, seed=23)
+    sc = scale_for(d)
+    o, lse = fa.fwd_fp8(bytes_to_dev(x["q8"]), bytes_to_dev(x["k8"]), to_dev(x["v"]),
+                        x["q_descale"], x["k_descale"], causal=True, softmax_scale=sc)
+    torch.cuda.synchronize()
+    b, h = 1, 7
+    sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+    ro, rlse = ora.attention_forward(x["q"][sl], x["k"][sl], x["v"][sl], sc, True)
+    errs = dict(o_excess=o_excess(to_host(o[b:b + 1, :, h:h + 1]), ro),
+                lse=max_abs(to_host(lse[b:b + 1, h:h + 1]), rlse))
+    say(f"whole head b={b} h={h} errors {errs}")
+    assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE
+    rng = np.random.Generator(np.random.PCG64(24))
+    rows = np.unique(np.r_[np.arange(32), np.arange(N - 32, N), rng.integers(0, N, 96)])
+    for (b, h) in ((0, 0), (0, 15), (1, 3), (1, 12)):
+        qh, kh, vh = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+        r_o, r_lse, _, _ = ora.head_query_rows(qh, kh, vh, np.zeros_like(vh), sc, True, rows)
+        e = dict(o_excess=o_excess(to_host(o[b, rows, h]), r_o),
+                 lse=max_abs(to_host(lse[b, h, rows]), r_lse))
+        say(f"rows b={b} h={h} errors {e}")
+        assert e["o_excess"] <= 1.0 and e["lse"] <= TOL_LSE
