@@ -60,6 +60,10 @@ DENSE_CASES = [
     (1, 260, 4, 1, 64),
     (1, 1024, 4, 2, 128),
     (1, 777, 2, 2, 128),
+    # query tile 7 (rows 224..) holds the last rows: the fast mode's stored
+    # tile 8m + 7 ends ragged
+    (1, 250, 2, 2, 128),
+    (2, 250, 3, 1, 64),
 ]
 
 
