@@ -27,7 +27,12 @@
 //    a packed sequence with Lq queries and Lk keys aligns the diagonal
 //    bottom-right (query i sees key j iff j <= i + Lk - Lq, the decode-shaped
 //    batches of [FA4B] 3.3.2), and a query that sees no key gets O = 0 and
-//    LSE = -inf.
+//    LSE = -inf;
+//  * fp8 scores (template flag FP8, dense only; [FA2] "Limitations and future
+//    work", [FA4C] 5.1): Q and K arrive as OCP e4m3 bytes, the K tile is
+//    copied as bytes, S^T takes d/64 fp8 32x32x64 products per 32 keys, and
+//    the descale factors of Q and K are folded into the exponent scale c;
+//    P, V and the P V product stay bf16.
 #include "fa_common.h"
 #include "fa_launch.h"
 
