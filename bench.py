@@ -244,6 +244,26 @@ def run_decode(args):
         "bwd_tflops": f_bwd / (ms["bwd_main"] * 1e-3) / 1e12,
         "visible_pairs_per_head": pairs, "nseq": len(lq), "total_q": Tq, "total_k": Tk,
     }
+    if args.extra and args.steps > 0:
+        # the forward with fp8 (e4m3) Q and K for the scores, per-tensor descale factors
+        qd = float(t["q"].float().abs().max()) / 448.0
+        kd = float(t["k"].float().abs().max()) / 448.0
+        q8 = (t["q"].float() / qd).to(torch.float8_e4m3fn)
+        k8 = (t["k"].float() / kd).to(torch.float8_e4m3fn)
+        for _ in range(3):
+            fa.varlen_qk_fwd_fp8(q8, k8, t["v"], cq, ck, qd, kd, causal=True,
+                                 softmax_scale=scale, workspace=wsf)
+        torch.cuda.synchronize()
+        fa.timing_begin()
+        for _ in range(args.steps):
+            fa.varlen_qk_fwd_fp8(q8, k8, t["v"], cq, ck, qd, kd, causal=True,
+                                 softmax_scale=scale, workspace=wsf)
+        kf = fa.timing_end()["fwd"]
+        fp8_ms = kf[1] / max(1, kf[0])
+        extras["fp8_fwd_kernel_ms"] = fp8_ms
+        extras["fp8_fwd_tflops"] = f_fwd / (fp8_ms * 1e-3) / 1e12
+        extras["fp8_fwd_speedup_vs_bf16"] = ms["fwd"] / fp8_ms
+        del q8, k8
     line = {
         "metric": DECODE_METRIC,
         "value": value,
@@ -304,7 +324,8 @@ def main():
     ap.add_argument("--traffic-file", default=TRAFFIC_FILE,
                     help="recorded HBM bytes per launch of the dominant kernel")
     ap.add_argument("--extra", action="store_true",
-                    help="also time the backward with the other dQ reduction modes (extras)")
+                    help="also time the backward with the other dQ reduction modes and the "
+                         "forward with fp8 scores (extras)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

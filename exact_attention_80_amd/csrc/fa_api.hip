@@ -267,19 +267,38 @@ int hip_fail(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 // shared implementations of dense and varlen calls
 
+// Scores from fp8 inputs: q and k hold OCP e4m3 bytes standing for
+// q_descale * Q and k_descale * K (fa_fwd_fp8, fa_varlen_qk_fwd_fp8).
+struct Fp8Scores {
+  bool on = false;
+  float q_descale = 1.f, k_descale = 1.f;
+};
+
 // cu / T: query offsets and tokens; cu_k / Tk: key offsets and tokens
 // (cu_k == cu and Tk == T for calls with equal lengths)
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, int B,
             int N, const int32_t* cu, const int32_t* cu_k, int nseq, long T, long Tk, int Hq,
-            int Hkv, int d, float scale, int causal, void* ws, size_t ws_bytes, void* stream) {
+            int Hkv, int d, float scale, int causal, void* ws, size_t ws_bytes, void* stream,
+            Fp8Scores f8 = Fp8Scores{}) {
   int st;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
-      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
+  if ((st = check_ptr(q, f8.on ? "q8" : "q")) || (st = check_ptr(k, f8.on ? "k8" : "k")) ||
+      (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
     return st;
   if (varlen && ((st = check_ptr(cu, "cu_seqlens_q")) || (st = check_ptr(cu_k, "cu_seqlens_k"))))
     return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
   if ((st = check_dims(Tk, Hq, Hkv, d, causal, scale))) return st;
+  float c = scale * fa::kLog2e;
+  if (f8.on) {
+    if (d != 64 && d != 128)
+      return fail(FA_ERR_UNSUPPORTED, "fp8 scores support head dimension 64 or 128");
+    if (!(f8.q_descale > 0.f) || !std::isfinite(f8.q_descale) || !(f8.k_descale > 0.f) ||
+        !std::isfinite(f8.k_descale))
+      return fail(FA_ERR_INVALID_ARG, "descale factors must be positive and finite");
+    c = scale * f8.q_descale * f8.k_descale * fa::kLog2e;
+    if (!std::isfinite(c) || !(c > 0.f))
+      return fail(FA_ERR_INVALID_ARG, "softmax_scale * q_descale * k_descale out of range");
+  }
   const FwdLayout lay = fwd_layout(varlen, nseq, T, Tk, Hq, d);
   if (ws_bytes < lay.total || (lay.total > 0 && !ws))
     return fail(FA_ERR_WORKSPACE, "workspace smaller than fa_*fwd_workspace_size()");
@@ -289,8 +308,13 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   FwdParams p{};
-  p.q = static_cast<const fa::bf16*>(q);
-  p.k = static_cast<const fa::bf16*>(k);
+  if (f8.on) {
+    p.q8 = static_cast<const uint8_t*>(q);
+    p.k8 = static_cast<const uint8_t*>(k);
+  } else {
+    p.q = static_cast<const fa::bf16*>(q);
+    p.k = static_cast<const fa::bf16*>(k);
+  }
   p.v = static_cast<const fa::bf16*>(v);
   p.o = static_cast<fa::bf16*>(o);
   p.lse = lse;
@@ -301,7 +325,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
   p.G = Hq / Hkv;
   p.T = (int)T;
   p.sched = sched_mode();
-  p.c = scale * fa::kLog2e;
+  p.c = c;
   const int br = fa::fwd_tile_rows(d);
   long grid;
   hipError_t e;
@@ -329,7 +353,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
   if (grid <= 0) return FA_OK;
   if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   const long tk = timing_start(0, s);
-  e = fa::launch_fwd(p, d, causal != 0, varlen, (int)grid, s);
+  e = f8.on ? fa::launch_fwd_fp8(p, d, causal != 0, varlen, (int)grid, s)
+            : fa::launch_fwd(p, d, causal != 0, varlen, (int)grid, s);
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   if (varlen) {
@@ -504,45 +529,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
                int Hq, int Hkv, int d, float softmax_scale, float q_descale, float k_descale,
                int causal, void* stream) {
   if (!dense_ok(B, N)) return fail(FA_ERR_INVALID_ARG, "B and N must be positive");
-  int st;
-  if ((st = check_ptr(q8, "q8")) || (st = check_ptr(k8, "k8")) || (st = check_ptr(v, "v")) ||
-      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
-    return st;
-  if ((st = check_dims((long)B * N, Hq, Hkv, d, causal, softmax_scale))) return st;
-  if (d != 64 && d != 128)
-    return fail(FA_ERR_UNSUPPORTED, "fp8 scores support head dimension 64 or 128");
-  if (!(q_descale > 0.f) || !std::isfinite(q_descale) || !(k_descale > 0.f) ||
-      !std::isfinite(k_descale))
-    return fail(FA_ERR_INVALID_ARG, "descale factors must be positive and finite");
-  const float c = softmax_scale * q_descale * k_descale * fa::kLog2e;
-  if (!std::isfinite(c) || !(c > 0.f))
-    return fail(FA_ERR_INVALID_ARG, "softmax_scale * q_descale * k_descale out of range");
-  std::string why;
-  if ((st = check_device(&why))) return fail(st, why);
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  FwdParams p{};
-  p.q8 = static_cast<const uint8_t*>(q8);
-  p.k8 = static_cast<const uint8_t*>(k8);
-  p.v = static_cast<const fa::bf16*>(v);
-  p.o = static_cast<fa::bf16*>(o);
-  p.lse = lse;
-  p.B = B;
-  p.N = N;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.G = Hq / Hkv;
-  p.T = (int)((long)B * N);
-  p.sched = sched_mode();
-  p.c = c;
-  p.nq = (int)cdiv(N, fa::fwd_tile_rows(d));
-  const long grid = (long)p.nq * B * Hq;
-  if (grid > 0x7fffffffL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
-  const long tk = timing_start(0, s);
-  const hipError_t e = fa::launch_fwd_fp8(p, d, causal != 0, (int)grid, s);
-  timing_stop(tk, s);
-  if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
-  return FA_OK;
+  return run_fwd(q8, k8, v, o, lse, false, B, N, nullptr, nullptr, 0, (long)B * N, (long)B * N,
+                 Hq, Hkv, d, softmax_scale, causal, nullptr, 0, stream,
+                 Fp8Scores{true, q_descale, k_descale});
 }
 
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
@@ -620,6 +609,19 @@ int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float
     return fail(FA_ERR_INVALID_ARG, "max_seqlen_q and max_seqlen_k must be >= 0");
   return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
                  Hq, Hkv, d, softmax_scale, causal, ws, ws_bytes, stream);
+}
+
+int fa_varlen_qk_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                         int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                         int Hkv, int d, float softmax_scale, float q_descale, float k_descale,
+                         int causal, void* ws, size_t ws_bytes, void* stream) {
+  if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
+  if (max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q and max_seqlen_k must be >= 0");
+  return run_fwd(q8, k8, v, o, lse, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
+                 total_k, Hq, Hkv, d, softmax_scale, causal, ws, ws_bytes, stream,
+                 Fp8Scores{true, q_descale, k_descale});
 }
 
 size_t fa_varlen_qk_bwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,

@@ -28,7 +28,7 @@
 //    bottom-right (query i sees key j iff j <= i + Lk - Lq, the decode-shaped
 //    batches of [FA4B] 3.3.2), and a query that sees no key gets O = 0 and
 //    LSE = -inf;
-//  * fp8 scores (template flag FP8, dense only; [FA2] "Limitations and future
+//  * fp8 scores (template flag FP8; [FA2] "Limitations and future
 //    work", [FA4C] 5.1): Q and K arrive as OCP e4m3 bytes, the K tile is
 //    copied as bytes, S^T takes d/64 fp8 32x32x64 products per 32 keys, and
 //    the descale factors of Q and K are folded into the exponent scale c;
@@ -433,12 +433,18 @@ hipError_t launch_fwd_t(const FwdParams& p, int grid, hipStream_t stream) {
 
 int fwd_tile_rows(int d) { return fwd_waves(d) * 32; }
 
-hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, int grid, hipStream_t stream) {
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool varlen, int grid,
+                          hipStream_t stream) {
   constexpr int NW = kFwdWaves;
-  if (d == 128)
-    return causal ? launch_fwd_t<128, NW, true, false, true>(p, grid, stream)
+  if (d == 128) {
+    if (causal) return varlen ? launch_fwd_t<128, NW, true, true, true>(p, grid, stream)
+                              : launch_fwd_t<128, NW, true, false, true>(p, grid, stream);
+    return varlen ? launch_fwd_t<128, NW, false, true, true>(p, grid, stream)
                   : launch_fwd_t<128, NW, false, false, true>(p, grid, stream);
-  return causal ? launch_fwd_t<64, NW, true, false, true>(p, grid, stream)
+  }
+  if (causal) return varlen ? launch_fwd_t<64, NW, true, true, true>(p, grid, stream)
+                            : launch_fwd_t<64, NW, true, false, true>(p, grid, stream);
+  return varlen ? launch_fwd_t<64, NW, false, true, true>(p, grid, stream)
                 : launch_fwd_t<64, NW, false, false, true>(p, grid, stream);
 }
 

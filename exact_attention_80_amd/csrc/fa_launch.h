@@ -49,9 +49,10 @@ int fwd_tile_keys();
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int grid,
                       hipStream_t stream);
 
-// Dense forward with fp8 (OCP e4m3) Q and K for the scores (p.q8, p.k8; p.c
+// Forward with fp8 (OCP e4m3) Q and K for the scores (p.q8, p.k8; p.c
 // includes their descale factors) and bf16 V; d = 64 or 128.
-hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, int grid, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool varlen, int grid,
+                          hipStream_t stream);
 
 // D = rowsum(dO o O) and LSE * log2(e) in the logsumexp layout; zeroes the
 // fp32 dQ accumulator (when given), the semaphores and the workspace header.

@@ -42,6 +42,7 @@ _SIGS = {
     "fa_varlen_bwd": ([_p] * 10 + [_i] * 6 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_varlen_qk_fwd_workspace_size": ([_i] * 7, _sz),
     "fa_varlen_qk_fwd": ([_p] * 7 + [_i] * 8 + [_f, _i, _p, _sz, _p], _i),
+    "fa_varlen_qk_fwd_fp8": ([_p] * 7 + [_i] * 8 + [_f, _f, _f, _i, _p, _sz, _p], _i),
     "fa_varlen_qk_bwd_workspace_size": ([_i] * 8, _sz),
     "fa_varlen_qk_bwd": ([_p] * 11 + [_i] * 8 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_workspace_error": ([_p, _sz, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
@@ -286,6 +287,35 @@ def varlen_qk_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
                                  _scale(d, softmax_scale), int(causal), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream()),
            "fa_varlen_qk_fwd")
+    return o, lse
+
+
+
+def varlen_qk_fwd_fp8(q8, k8, v, cu_seqlens_q, cu_seqlens_k, q_descale: float, k_descale: float,
+                      causal: bool = False, softmax_scale: float | None = None,
+                      max_seqlen_q: int = 0, max_seqlen_k: int = 0,
+                      workspace: torch.Tensor | None = None):
+    """varlen_qk_fwd with fp8 scores: q8 [Tq,Hq,d], k8 [Tk,Hkv,d] OCP e4m3 bytes
+    (uint8 or float8_e4m3fn) standing for q_descale * q8 and k_descale * k8, v
+    [Tk,Hkv,d] bf16 -> (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32).  d = 64 or 128."""
+    Tq, Hq, d = q8.shape
+    Tk, Hkv = k8.shape[0], k8.shape[1]
+    q8 = _e4m3_bytes(q8, "q8", (Tq, Hq, d))
+    k8 = _e4m3_bytes(k8, "k8", (Tk, Hkv, d))
+    _need(v, "v", (Tk, Hkv, d))
+    nseq = _cu_pair(cu_seqlens_q, cu_seqlens_k)
+    o = torch.empty((Tq, Hq, d), dtype=torch.bfloat16, device=v.device)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=v.device)
+    ws = workspace
+    if ws is None:
+        ws = varlen_qk_fwd_workspace(nseq, Tq, Tk, Hq, Hkv, d, causal, v.device)
+    ws_n = 0 if ws is None else ws.numel()
+    _check(_lib.fa_varlen_qk_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), cu_seqlens_q.data_ptr(),
+                                     cu_seqlens_k.data_ptr(), nseq, Tq, Tk, int(max_seqlen_q),
+                                     int(max_seqlen_k), Hq, Hkv, d, _scale(d, softmax_scale),
+                                     float(q_descale), float(k_descale), int(causal), _ptr(ws),
+                                     ws_n, _stream()), "fa_varlen_qk_fwd_fp8")
     return o, lse
 
 

@@ -25,7 +25,8 @@ Recipe:
     quantised per tensor to OCP e4m3 ("fn": largest finite 448, no
     infinities) with descale = amax(|x|) / 448 in float32 and bytes
     e4m3(x / descale), rounded to nearest, ties to even; V is bf16-rounded.
-    The attention inputs the bytes stand for are descale * e4m3 value.
+    The attention inputs the bytes stand for are descale * e4m3 value; the
+    packed variant quantises the packed draws the same way.
 """
 
 from __future__ import annotations
@@ -119,16 +120,18 @@ def qk_lengths(total_k: int = 65536, lo: int = 128, hi: int = 16384, seed: int =
     return lq, lk
 
 
-def varlen_qk_inputs(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, seed: int = 0) -> dict:
-    """Packed Q, dO [Tq, Hq, d] and K, V [Tk, Hkv, d] ~ N(0, 1), bf16-rounded,
-    plus cu_seqlens_q and cu_seqlens_k."""
+def varlen_qk_inputs(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, seed: int = 0,
+                     round_bf16: bool = True) -> dict:
+    """Packed Q, dO [Tq, Hq, d] and K, V [Tk, Hkv, d] ~ N(0, 1), bf16-rounded
+    unless asked not to, plus cu_seqlens_q and cu_seqlens_k."""
     if len(lengths_q) != len(lengths_k):
         raise ValueError("one query length and one key length per sequence")
     tq, tk = int(np.sum(lengths_q)), int(np.sum(lengths_k))
     g = np.random.Generator(np.random.PCG64(seed))
     out = {}
     for name, t, h in (("q", tq, Hq), ("k", tk, Hkv), ("v", tk, Hkv), ("do", tq, Hq)):
-        out[name] = bf16_round(g.standard_normal((t, h, d), dtype=np.float32))
+        a = g.standard_normal((t, h, d), dtype=np.float32)
+        out[name] = bf16_round(a) if round_bf16 else a
     out["cu_seqlens_q"] = cu_seqlens(lengths_q)
     out["cu_seqlens_k"] = cu_seqlens(lengths_k)
     return out
@@ -200,3 +203,16 @@ def fp8_dense_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, seed: int = 0) -
     return {"q8": q8, "k8": k8, "q_descale": qd, "k_descale": kd,
             "q": qd * e4m3_decode(q8), "k": kd * e4m3_decode(k8),
             "v": bf16_round(raw["v"])}
+
+
+def fp8_varlen_qk_inputs(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, seed: int = 0) -> dict:
+    """Packed fp8-score inputs with separate query and key lengths: the draws
+    of varlen_qk_inputs before bf16 rounding, Q and K quantised per tensor as
+    in fp8_dense_inputs, V bf16-rounded, plus the offsets."""
+    raw = varlen_qk_inputs(lengths_q, lengths_k, Hq, Hkv, d, seed, round_bf16=False)
+    q8, qd = quantize_e4m3(raw["q"])
+    k8, kd = quantize_e4m3(raw["k"])
+    return {"q8": q8, "k8": k8, "q_descale": qd, "k_descale": kd,
+            "q": qd * e4m3_decode(q8), "k": kd * e4m3_decode(k8),
+            "v": bf16_round(raw["v"]),
+            "cu_seqlens_q": raw["cu_seqlens_q"], "cu_seqlens_k": raw["cu_seqlens_k"]}

@@ -24,7 +24,8 @@
  * ---------------------------------------
  *  - Tensors are caller-owned DEVICE memory (e.g. PyTorch allocations), dense,
  *    contiguous, 16-byte aligned.  Q, K, V, O, dO, dQ, dK, dV are bf16
- *    (fa_fwd_fp8 alone takes Q and K as one-byte e4m3 values).
+ *    (fa_fwd_fp8 and fa_varlen_qk_fwd_fp8 take Q and K as one-byte e4m3
+ *    values).
  *    The library never allocates or frees device memory.  Its only host state
  *    is a per-device property cache and the opt-in timing event pool below,
  *    so calls on different streams are independent as long as their buffers
@@ -38,7 +39,7 @@
  *    non-decreasing) and a violation is reported through the workspace error
  *    word (fa_workspace_error), not by the return value.
  *  - d (head dimension) is 64, 128 or 256 (256: the fa_bwd partial-tile modes
- *    deterministic == 2, 3 are not offered; fa_fwd_fp8 takes 64 or 128).
+ *    deterministic == 2, 3 are not offered; the fp8 forwards take 64 or 128).
  *    Hq must be a positive multiple of Hkv;
  *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
  *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2)
@@ -221,6 +222,18 @@ int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float
                      int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
                      int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* fa_varlen_qk_fwd with fp8 scores, as in fa_fwd_fp8: q8 [total_q, Hq, d] and
+ * k8 [total_k, Hkv, d] are OCP e4m3 bytes standing for q_descale * Q and
+ * k_descale * K; v, o, lse, the offsets and the bottom-right causal mask as in
+ * fa_varlen_qk_fwd; d = 64 or 128.  The workspace is sized by
+ * fa_varlen_qk_fwd_workspace_size (the same layout).  The decode-shaped
+ * batches of [FA4B] 3.3.2 with an fp8 key cache are the intended use. */
+int fa_varlen_qk_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                         int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                         int Hkv, int d, float softmax_scale, float q_descale, float k_descale,
+                         int causal, void* ws, size_t ws_bytes, void* stream);
 
 /* deterministic must be 0 or 1 (2 or 3 returns FA_ERR_UNSUPPORTED); the size
  * query returns 0 for invalid sizes or modes. */

@@ -36,6 +36,7 @@ def lib():
     L.fa_varlen_bwd_workspace_size.argtypes = [i] * 7
     L.fa_varlen_bwd_workspace_size.restype = sz
     L.fa_varlen_qk_fwd.argtypes = [p] * 7 + [i] * 8 + [f, i, p, sz, p]
+    L.fa_varlen_qk_fwd_fp8.argtypes = [p] * 7 + [i] * 8 + [f, f, f, i, p, sz, p]
     L.fa_varlen_qk_bwd.argtypes = [p] * 11 + [i] * 8 + [f, i, i, p, sz, p]
     L.fa_varlen_qk_fwd_workspace_size.argtypes = [i] * 7
     L.fa_varlen_qk_fwd_workspace_size.restype = sz
@@ -55,7 +56,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_varlen_qk_fwd",
+    for n in ("fa_fwd", "fa_fwd_fp8", "fa_varlen_qk_fwd_fp8", "fa_bwd", "fa_varlen_fwd", "fa_varlen_bwd", "fa_varlen_qk_fwd",
               "fa_varlen_qk_bwd", "fa_fwd_workspace_size",
               "fa_bwd_workspace_size", "fa_status_string", "fa_workspace_error"):
         assert n in names
@@ -223,3 +224,20 @@ def test_binding_has_no_fallback():
     src = open(os.path.join(ROOT, "exact_attention_80_amd", "fa.py")).read()
     assert "oracle" not in src
     assert "numpy" not in src
+
+
+def test_varlen_qk_fwd_fp8_rejects_bad_arguments(lib):
+    ws_n = lib.fa_varlen_qk_fwd_workspace_size(2, 100, 3000, 4, 2, 128, 1)
+    assert ws_n > 0
+
+    def call(q8=P, cuq=P, ws=P, nbytes=ws_n, d=128, qd=0.01, kd=0.02, nseq=2):
+        return lib.fa_varlen_qk_fwd_fp8(q8, P, P, P, P, cuq, P, nseq, 100, 3000, 0, 0, 4, 2, d,
+                                        0.125, qd, kd, 1, ws, nbytes, None)
+    assert call(q8=None) == INVALID
+    assert call(cuq=None) == INVALID
+    assert call(nseq=0) == INVALID
+    assert call(qd=0.0) == INVALID
+    assert call(kd=float("inf")) == INVALID
+    assert call(d=256) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=16) == WORKSPACE

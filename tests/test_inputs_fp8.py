@@ -73,3 +73,18 @@ def test_fp8_inputs_recipe():
     assert np.max(x["q8"] & 0x7F) == 0x7E
     assert np.allclose(x["q"], raw["q"], rtol=2.0 ** -4, atol=x["q_descale"] * 2.0 ** -9)
     assert np.array_equal(x["v"], inputs.bf16_round(raw["v"]))
+
+
+def test_fp8_packed_inputs_recipe():
+    lq, lk = [1, 5, 0], [40, 5, 9]
+    x = inputs.fp8_varlen_qk_inputs(lq, lk, 4, 2, 64, seed=8)
+    raw = inputs.varlen_qk_inputs(lq, lk, 4, 2, 64, seed=8, round_bf16=False)
+    assert x["q8"].shape == (6, 4, 64) and x["k8"].shape == (54, 2, 64)
+    assert np.array_equal(x["cu_seqlens_q"], [0, 1, 6, 6])
+    assert np.array_equal(x["cu_seqlens_k"], [0, 40, 45, 54])
+    assert x["k_descale"] == np.float32(np.abs(raw["k"]).max() / 448)
+    assert np.array_equal(x["q"], x["q_descale"] * inputs.e4m3_decode(x["q8"]))
+    assert np.array_equal(x["v"], inputs.bf16_round(raw["v"]))
+    # the bf16-rounded draws are the same numbers rounded
+    assert np.array_equal(inputs.varlen_qk_inputs(lq, lk, 4, 2, 64, seed=8)["k"],
+                          inputs.bf16_round(raw["k"]))

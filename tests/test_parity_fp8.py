@@ -1,5 +1,6 @@
-"""GPU parity of the fp8-score forward: Q and K arrive as OCP e4m3 bytes with
-per-tensor descale factors, V as bf16.  The oracle runs the fp64 forward on
+"""GPU parity of the fp8-score forwards (dense, and packed with separate query
+and key lengths): Q and K arrive as OCP e4m3 bytes with per-tensor descale
+factors, V as bf16.  The oracle runs the fp64 forward on
 the values the bytes stand for (descale * decoded value), so the only
 differences left are the kernel's accumulation and its bf16 P and O, as for
 the bf16 forward, and the same tolerances apply at the scale of these inputs.
@@ -115,3 +116,49 @@ def test_fp8_forward_full_size(fa):
                  lse=max_abs(to_host(lse[b, h, rows]), r_lse))
         say(f"rows b={b} h={h} errors {e}")
         assert e["o_excess"] <= 1.0 and e["lse"] <= TOL_LSE
+
+
+def lse_error(lse, ref) -> float:
+    """Max |LSE - LSE*| over rows that see a key; rows that see none must be
+    -inf on both sides (returns inf otherwise)."""
+    empty = np.isneginf(ref)
+    if not np.array_equal(np.isneginf(lse), empty):
+        return float("inf")
+    return float(np.max(np.abs(lse[~empty] - ref[~empty]))) if np.any(~empty) else 0.0
+
+
+FP8_QK_CASES = [
+    # (query lengths, key lengths, Hq, Hkv, d): decode rows and short chunks,
+    # more queries than keys, empty sequences, split one-query tiles (more
+    # than 32 key tiles of 64), chunked prefill
+    ([1, 1, 3, 1, 17], [700, 33, 1029, 1, 260], 8, 2, 128),
+    ([300, 64, 5, 40], [100, 64, 1, 700], 2, 2, 64),
+    ([0, 7, 129, 1], [50, 0, 513, 257], 4, 1, 128),
+    ([1, 17, 33, 289], [5000, 2049, 5000, 2100], 4, 2, 128),
+    ([1, 3], [9000, 4100], 2, 1, 64),
+    ([256, 257, 31], [1000, 600, 31], 4, 4, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", FP8_QK_CASES, ids=lambda c: f"n{len(c[0])}h{c[2]}{c[3]}d{c[4]}")
+def test_fp8_varlen_qk_forward_parity(fa, case, causal):
+    import torch
+    lq, lk, Hq, Hkv, d = case
+    say(f"fp8 varlen_qk lq={lq} lk={lk} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    x = inputs.fp8_varlen_qk_inputs(lq, lk, Hq, Hkv, d, seed=len(lq) + d)
+    cq = torch.from_numpy(x["cu_seqlens_q"]).to("cuda")
+    ck = torch.from_numpy(x["cu_seqlens_k"]).to("cuda")
+    sc = scale_for(d)
+    o, lse = fa.varlen_qk_fwd_fp8(bytes_to_dev(x["q8"]), bytes_to_dev(x["k8"]), to_dev(x["v"]),
+                                  cq, ck, x["q_descale"], x["k_descale"], causal=causal,
+                                  softmax_scale=sc)
+    o, lse = to_host(o), to_host(lse)
+    ro, rlse = ora.varlen_qk_forward(x["q"], x["k"], x["v"], x["cu_seqlens_q"],
+                                     x["cu_seqlens_k"], sc, causal)
+    errs = dict(o_excess=o_excess(o, ro), lse=lse_error(lse, rlse))
+    say(f"errors {errs}")
+    assert np.all(np.isfinite(o))
+    assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE
+    empty = np.isneginf(rlse).T  # [Tq, Hq]: rows that see no key are exactly zero
+    assert np.all(o[empty] == 0.0)
