@@ -9,7 +9,11 @@
 //  * K and V tiles of 64 keys are copied global->LDS by direct loads (no
 //    register staging) into padded tiles, through a ring of fwd_stages(D)
 //    buffers (4; 2 for d = 256, whose workgroups have 4 waves): the next
-//    tiles are in flight while tile j is computed;
+//    tiles are in flight while tile j is computed; with 8 waves the first
+//    four issue all copies, after their own products of a tile (they run
+//    ahead of their SIMD partners, which are the critical path);
+//  * a tile's K operands (and the first V^T operands) are read into
+//    registers in one batch before its products;
 //  * the score tile is computed transposed, S^T = K Q^T, so each lane holds one
 //    query column: the row max and row sum are in-lane plus one exchange
 //    between lane halves;
@@ -122,6 +126,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using VT = SwzTile<kBC, CH, D == 256 ? 36 : (D == 128 ? 20 : 12)>;
 
   constexpr int STAGES = fwd_stages(D);          // K/V tiles in flight or in use
+  // bf16 operands of a tile's products are read in bulk ahead of them (the
+  // d = 256 and fp8 variants keep the interleaved reads)
+  constexpr bool PREFETCH = !FP8 && D <= 128;
   __shared__ __attribute__((aligned(16))) char kv_s[STAGES][KT::kBytes + VT::kBytes];
 
   WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
@@ -186,16 +193,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   // ---- direct global->LDS copy of one K and one V tile.  Rows past the
   // sequence end arrive as zeros (buffer range check); their scores are
-  // masked.  Every wave issues the same number of copies per tile (kCopies).
+  // masked.  With 8 waves only waves 0-3 copy, each the same number of
+  // instructions per tile (kCopies), and they issue a tile's copies after
+  // their own products of the previous tile: the two waves of a SIMD share
+  // its matrix unit, the older one (waves 0-3) gets ahead and would otherwise
+  // wait at the next barrier, so the copies cost the critical waves 4-7
+  // nothing.  The 2-deep ring (d = 256) copies right after the barrier
+  // instead, so each tile has a whole tile of products to arrive.
   constexpr int VST = D == 256 ? 36 : (D == 128 ? 20 : 12);
-  constexpr int kCopies = dma_count<KT, NW>() + dma_count<VT, NW>();
+  constexpr int CW = NW == 8 ? NW / 2 : NW;      // waves that copy
+  constexpr bool LATE = STAGES >= 3;             // copies after the products
+  constexpr int kCopies = dma_count<KT, CW>() + dma_count<VT, CW>();
+  const bool copier = wave < CW;
   const long kv_bytes = kv_row * 2;     // V row pitch (bf16)
   const long k_bytes = kv_row * EB;     // K row pitch
-  TileCopy<KT, NW> kcopy;
-  TileCopy<VT, NW> vcopy;
-  kcopy.init(k_bytes, KCH + 1, wave, lane, [](int, int pc) { return pc < KCH ? pc : -1; });
-  vcopy.init(kv_bytes, VST, wave, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
+  TileCopy<KT, CW> kcopy;
+  TileCopy<VT, CW> vcopy;
+  kcopy.init(k_bytes, KCH + 1, wave % CW, lane, [](int, int pc) { return pc < KCH ? pc : -1; });
+  vcopy.init(kv_bytes, VST, wave % CW, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
   auto issue_tile = [&](int u) {  // the u-th tile of this item, key tile jb + u
+    if (!copier) return;
     char* kt = kv_s[u % STAGES];
     const int j = jb + u;
     kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * k_bytes,
@@ -218,10 +235,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int v_tr[2] = {VT::off(4 * (g16 >> 1) + (L16 >> 2), 16 * (g16 & 1) + 4 * (L16 & 3)),
                        VT::off(8 + 4 * (g16 >> 1) + (L16 >> 2), 16 * (g16 & 1) + 4 * (L16 & 3))};
 
-  auto compute_tile = [&](int j, const char* kt, const char* vt) {
-    const int key0 = j * kBC;
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
+  // S^T = K Q^T for the two 32-key blocks of key tile j
+  auto scores_tile = [&](const char* kt, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -238,6 +253,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
           s[kb] = mfma32x32x64_fp8(a, qf8[dc], s[kb]);
         }
       }
+    } else if (PREFETCH) {
+      // every K operand of the tile is read before the first product, so the
+      // products wait on one LDS latency instead of one per product pair
+      bf16x8 kf[D / 16][2];
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          kf[dc][kb] = as_bf16x8(ld_lds16(kt + KT::off(kb * 32 + l32, 16 * dc + 8 * half)));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[dc][kb], qf[dc], s[kb]);
     } else {
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
@@ -247,6 +276,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
           s[kb] = mfma32x32x16(a, qf[dc], s[kb]);
         }
       }
+    }
+  };
+  // masked online softmax and O^T += V^T P^T for key tile j
+  auto finish_tile = [&](int j, const char* vt, f32x16 (&s)[2]) {
+    const int key0 = j * kBC;
+    // V^T operands of the first two 16-key chunks are read now, so their
+    // latency hides behind the mask, the row max and the rescale
+    bf16x8 vpre[2][D / 32];
+    if (PREFETCH) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int vo = 16 * kc * VT::kPitch + 64 * db;
+          vpre[kc][db] = cat8(ld_lds_tr8(vt + v_tr[0] + vo), ld_lds_tr8(vt + v_tr[1] + vo));
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
     const bool need_mask = (CAUSAL && key0 + kBC - 1 > wq0 + off) || (key0 + kBC > klen);
     if (need_mask) {
@@ -294,17 +340,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       const bf16x8 pb = frag_rows(s[kc >> 1], kc & 1);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int vo = 16 * kc * VT::kPitch + 64 * db;
-        const u32x2 lo = ld_lds_tr8(vt + v_tr[0] + vo);
-        const u32x2 hi = ld_lds_tr8(vt + v_tr[1] + vo);
-        oacc[db] = mfma32x32x16(cat8(lo, hi), pb, oacc[db]);
+        bf16x8 va;
+        if (PREFETCH && kc < 2) {
+          va = vpre[kc][db];
+        } else {
+          const int vo = 16 * kc * VT::kPitch + 64 * db;
+          va = cat8(ld_lds_tr8(vt + v_tr[0] + vo), ld_lds_tr8(vt + v_tr[1] + vo));
+        }
+        oacc[db] = mfma32x32x16(va, pb, oacc[db]);
       }
     }
   };
+  auto compute_tile = [&](int j, const char* kt, const char* vt) {
+    f32x16 s[2];
+    scores_tile(kt, s);
+    finish_tile(j, vt, s);
+  };
 
-  // STAGES-deep copy ring: tiles j+1 .. j+STAGES-1 are in flight while tile j
-  // is computed.  Copies retire in issue order, so waiting until at most
-  // (tiles issued after j) x kCopies copies are outstanding means tile j is in.
+  // STAGES-deep copy ring: tiles j+1 .. j+STAGES-2 (and j+STAGES-1 once it is
+  // issued) are in flight while tile j is computed.  Copies retire in issue
+  // order, so waiting until at most (tiles issued after j) x kCopies copies
+  // are outstanding means tile j is in (waves that do not copy pass at once;
+  // the barrier makes the copiers' tiles visible to them).
   wait_vmem();  // Q fragments
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
@@ -316,13 +373,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     else if (newer == 1) wait_vmem_leave<kCopies>();
     else wait_vmem();
     lds_barrier();  // tile u landed for every wave; tile u-1's buffer is free
-    if (u + STAGES - 1 < nt) issue_tile(u + STAGES - 1);
+    if (!LATE && u + STAGES - 1 < nt) issue_tile(u + STAGES - 1);
     const char* kt = kv_s[u % STAGES];
     // a wave whose rows are all past the sequence end, or (causal) all above
     // this tile's first key, would only add exact zeros: it skips the tile
     // (it still copies and meets every barrier)
     const bool live = wq0 < wi.seq_len && (!CAUSAL || j * kBC <= wq0 + 31 + off);
     if (live) compute_tile(j, kt, kt + KT::kBytes);
+    // (late) tile u+STAGES-1 goes into tile u-1's slot, which every wave left
+    // before the barrier above
+    if (LATE && u + STAGES - 1 < nt) issue_tile(u + STAGES - 1);
   }
 
   // ---- epilogue: O = O~ / l (single final rescale), LSE = (m + log2 l) ln 2;
