@@ -17,6 +17,10 @@ Prints one JSON line.  Besides the headline it carries:
                 MFMA peak; `traffic` is the kernel's HBM bytes per launch from
                 the recorded rocprofv3 counter runs (profiles/), or null when
                 the kernel sources changed since they were taken;
+  extras        per-kernel times; in the atomic mode also the bytes of fp32 dQ
+                atomic adds per backward launch and the rate they imply
+                (device-scope fp32 atomics, not the matrix unit, bound that
+                kernel);
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample (whole query
                 heads of the same workload) on this host's cores, scaled to the
                 metric's unit.
@@ -71,6 +75,19 @@ def measured_traffic(path: str, config: dict):
     if rec.get("source_sha256") != kernel_source_hash() or rec.get("config") != config:
         return None
     return rec.get("bytes_per_launch")
+
+
+def dq_reduction_bytes(B, N, Hq, d, causal):
+    """fp32 bytes the backward main kernel adds into the dQ accumulator per launch:
+    one 32-row x d tile per (query tile, key tile) pair the causal mask leaves
+    visible, key tiles of 256 keys (128 for d = 256)."""
+    bq, bc = 32, (128 if d == 256 else 256)
+    nq, nkv = -(-N // bq), -(-N // bc)
+    if causal:
+        pairs = sum(min(nkv, (i * bq + bq - 1) // bc + 1) for i in range(nq))
+    else:
+        pairs = nq * nkv
+    return pairs * B * Hq * bq * d * 4
 
 
 def make_inputs(B, N, Hq, Hkv, d, seed=0):
@@ -404,6 +421,12 @@ def main():
         "bwd_tflops": f_bwd / ((ms_bwd + ms_pre + ms_post) / max(1, n_bwd) * 1e-3) / 1e12,
         "pct_of_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
     }
+    if det == 0:
+        # the fast mode's dQ reduction: device-scope fp32 atomic adds, whose
+        # throughput (not the matrix unit) bounds the backward main kernel
+        dq_bytes = dq_reduction_bytes(B, N, Hq, d, causal)
+        extras["bwd_dq_atomic_bytes"] = dq_bytes
+        extras["bwd_dq_atomic_tbps"] = dq_bytes / (avg_bwd_ms * 1e-3) / 1e12
     if args.extra:
         o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
         this_ms = (ms_bwd + ms_pre + ms_post) / max(1, n_bwd)
