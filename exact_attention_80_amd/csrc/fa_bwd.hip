@@ -295,6 +295,20 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   }
 
   // dQ of item `item` from its dS^T (all waves' rows), reduced into dq_acc
+  // ordered mode: the semaphores of the dQ tiles whose adds this workgroup
+  // issued one item ago (pend_old) and in the current item (pend_sem).  A
+  // tile's semaphore is released only once its adds are known to be
+  // performed: the wait at the top of item t covers every memory operation
+  // issued before item t's copies, so it completes the adds issued two items
+  // earlier, and the barrier after it makes that true for every wave.
+  int* pend_sem = nullptr;
+  int* pend_old = nullptr;
+  auto release = [&](int*& sp) {
+    if (DET && sp != nullptr) {
+      if (tid == 0) __hip_atomic_fetch_add(sp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sp = nullptr;
+    }
+  };
   auto dq_item = [&](int item, const char* dss) {
     const int hh = item / nsteps;
     const int i = step_tile(item - hh * nsteps);
@@ -362,13 +376,13 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
                                                (((wave * NQB + qb) * 64 + lane) * 16), 0, kCoherent);
       return;
     }
-    if (!DET) {
-      // exactly 4 NQB atomic instructions per wave, so the next item can wait
-      // for its copies alone: they go through a buffer descriptor whose range
-      // ends at the tile's last valid row, and the hardware drops the ones
-      // for rows past the sequence end (no traffic, and no pile-up of many
-      // workgroups' adds on one clamped address when a sequence has a single
-      // query)
+    // exactly 4 NQB NCB atomic instructions per wave, so the next item can
+    // wait for its copies alone: they go through a buffer descriptor whose
+    // range ends at the tile's last valid row, and the hardware drops the ones
+    // for rows past the sequence end (no traffic, and no pile-up of many
+    // workgroups' adds on one clamped address when a sequence has a single
+    // query).  Relaxed device-scope adds, performed where every XCD sees them.
+    auto issue_atomics = [&]() {
       const int nvalid = min(BQ, it.q_len - q0);
       const float* tile0 = p.dq_acc + ((long)it.q_start + q0) * q_row + (long)h * D;
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -387,8 +401,10 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
           for (int r = 0; r < 4; ++r)
             (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
                 acc[c * NQB + qb][r], rsrc, vo + (16 * qb + r) * row_bytes + 64 * c, 0, 0);
+    };
+    if (!DET) {
+      issue_atomics();
     } else {
-      float* dq_base = p.dq_acc + (long)it.q_start * q_row + (long)h * D + dh0 + dblk * 16 + L16;
       // ordered reduction: writers of a dQ tile apply in descending key-tile order
       const int jhi = CAUSAL ? min(it.nkv - 1, (q0 + BQ - 1 + it.off) / BC) : it.nkv - 1;
       const int rank = jhi - it.jt;
@@ -419,21 +435,11 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
         }
       }
       __syncthreads();
-#pragma unroll
-      for (int c = 0; c < NCB; ++c)
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = q0 + 16 * (qb0 + qb) + 4 * g16 + r;
-            if (q < it.q_len)
-              __hip_atomic_fetch_add(dq_base + (long)q * q_row + 16 * c, acc[c * NQB + qb][r],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-      // every add of this workgroup has been performed before the release
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(semp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      issue_atomics();
+      // released two items later, once these adds are performed (see
+      // pend_old).  Deferring cannot create a cycle: a writer only ever
+      // waits for writers of higher key tiles, which never wait for it.
+      pend_sem = semp;
     }
   };
 
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   // or stores of the dQ issued in the previous item (4 NQB or NQB per wave)
   // were issued after them, so those stay in flight.
   auto wait_copies = [&](int item) {
-    if (DQM == kDqAtomic && item >= 2) wait_vmem_leave<4 * NQB * NCB>();
+    if ((DQM == kDqAtomic || DET) && item >= 2) wait_vmem_leave<4 * NQB * NCB>();
     else if (PARTS && item >= 2) wait_vmem_leave<NQB>();
     else wait_vmem();
     lds_barrier();
@@ -607,6 +613,11 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   if (nitems > 0) issue_item(0, q_s0, do_s0, st_s0);
   for (int item = 0; item < nitems; ++item) {
     wait_copies(item);
+    if (DET) {
+      release(pend_old);  // its adds were issued before this item's copies
+      pend_old = pend_sem;
+      pend_sem = nullptr;
+    }
     if (FUSED) {
       // the partial tile of item-3 is complete in every wave (its stores
       // were issued before copies this wait covered); item-4 was counted
@@ -625,8 +636,16 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
     compute_item(item, qs, dos, sts, odd ? ds_s1 : ds_s0);
   }
   if (nitems > 0) {
-    lds_barrier();  // the last item's dS^T is complete
+    if (DET) wait_vmem();  // every add issued so far is performed ...
+    lds_barrier();         // ... in every wave; the last item's dS^T is complete
+    release(pend_old);
+    release(pend_sem);
     dq_item(nitems - 1, (nitems - 1) & 1 ? ds_s1 : ds_s0);
+    if (DET) {
+      wait_vmem();
+      __syncthreads();
+      release(pend_sem);
+    }
   }
   if (FUSED && nitems > 0) {
     wait_vmem();    // every partial tile of this workgroup is stored
