@@ -53,13 +53,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.txt")
 KERNEL_SOURCES = ("fa_bwd.hip", "fa_common.h", "fa_launch.h")
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (so that editing a
+    comment does not mark the recorded counters as stale)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the sources the backward main kernel is built from."""
+    """sha256 over the code (comments stripped) of the sources the backward
+    main kernel is built from."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "exact_attention_80_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_80_amd", "csrc", name)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -18,7 +18,8 @@
 //    The dQ tile is reduced across key tiles either with fp32 device atomics
 //    (fast) or, in deterministic mode, in a fixed order: for each dQ tile the
 //    writers are applied in descending key-tile index, each waiting on a
-//    per-tile semaphore until its rank comes up, adding, then releasing.
+//    per-tile semaphore until its rank comes up, adding, and releasing it
+//    once its adds are known to be performed (two items later).
 //    Workgroups take their work items from an atomic ticket in that same
 //    descending order, so every workgroup a writer waits for already runs and
 //    the causal walk (diagonal first) never stalls on its first write.

@@ -44,3 +44,8 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_code_only_drops_comments_and_blank_lines():
+    src = "int a;  // note\n\n/* block\n comment */ int b;\nconst char* s = 0;\n"
+    assert bench.code_only(src) == "int a;\n int b;\nconst char* s = 0;"
