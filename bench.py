@@ -113,38 +113,53 @@ def make_inputs(B, N, Hq, Hkv, d, seed=0):
     return out
 
 
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity)."""
+    return len(os.sched_getaffinity(0))
+
+
+def blas_threads(n: int):
+    """Context that runs the oracle's BLAS with n threads (threadpoolctl when
+    present, else whatever the environment set)."""
+    try:
+        import threadpoolctl
+        return threadpoolctl.threadpool_limits(limits=n)
+    except Exception:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
 def cpu_baseline(B, N, Hq, Hkv, d, causal, budget_s):
-    """Oracle fwd+bwd on whole query heads until budget_s elapses (at least one head)."""
+    """Oracle fwd+bwd on whole query heads of the workload's shape until
+    budget_s elapses (at least one head), on every core of this process's
+    affinity; the rate is scaled by the algorithmic FLOPs per head."""
     import numpy as np
 
     from exact_attention_80_amd import inputs
     from oracle import attention as ora
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:  # pragma: no cover
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    cores = host_cores()
     scale = 1.0 / math.sqrt(d)
     g = np.random.Generator(np.random.PCG64(123))
     heads = 0
-    t0 = time.perf_counter()
-    while True:
-        qh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
-        kh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
-        vh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
-        doh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
-        ora.head_forward_backward(qh, kh, vh, doh, scale, causal)
-        heads += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or heads >= B * Hq:
-            break
+    with blas_threads(cores):
+        t0 = time.perf_counter()
+        while True:
+            qh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+            kh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+            vh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+            doh = inputs.bf16_round(g.standard_normal((N, d), dtype=np.float32))
+            ora.head_forward_backward(qh, kh, vh, doh, scale, causal)
+            heads += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or heads >= B * Hq:
+                break
     f, b = flops(1, N, 1, d, causal)
     tflops = heads * (f + b) / el / 1e12
     return {
-        "value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{heads} of {B * Hq} query heads (N={N}, d={d}, causal) fwd+bwd in fp64, "
-                  f"{el:.1f} s; rate scaled by algorithmic FLOPs per head",
+        "value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"{heads} of {B * Hq} query heads (N={N}, d={d}, "
+                  f"{'causal' if causal else 'non-causal'}) fwd+bwd in fp64, {el:.1f} s; "
+                  f"rate scaled by algorithmic FLOPs per head",
     }
 
 
@@ -173,16 +188,14 @@ def decode_cpu_baseline(x, lq, lk, Hq, Hkv, d, budget_s):
     import numpy as np
 
     from oracle import attention as ora
-    try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = host_cores()
     G = Hq // Hkv
     cq, ck = x["cu_seqlens_q"], x["cu_seqlens_k"]
     scale = 1.0 / math.sqrt(d)
     done_flops = 0.0
     units = 0
+    limit = blas_threads(threads)
+    limit.__enter__()
     t0 = time.perf_counter()
     for s in range(len(lq)):
         qa, qe, ka, ke = int(cq[s]), int(cq[s + 1]), int(ck[s]), int(ck[s + 1])
@@ -200,6 +213,7 @@ def decode_cpu_baseline(x, lq, lk, Hq, Hkv, d, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
+    limit.__exit__(None, None, None)
     return {
         "value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{units} of {len(lq) * Hkv} (sequence, key/value head group) slices of the "
@@ -328,6 +342,264 @@ def run_decode(args):
     print(json.dumps(line), flush=True)
 
 
+def measure_dense(fa, x, B, N, Hq, Hkv, d, causal, det, steps, warmup):
+    """Time `steps` forward+backward steps on resident inputs; returns the wall
+    time per step and the average of every kernel's HIP-event time (ms)."""
+    import torch
+    scale = 1.0 / math.sqrt(d)
+    ws = fa.bwd_workspace(x["q"], x["k"], causal, det)
+
+    def step():
+        o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
+        fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, softmax_scale=scale,
+               deterministic=det, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    fa.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = fa.timing_end()
+    del ws
+    avg = {k: v[1] / max(1, v[0]) for k, v in kt.items()}
+    avg["bwd_total"] = sum(kt[k][1] for k in ("bwd_pre", "bwd_main", "bwd_post")) / max(
+        1, kt["bwd_main"][0])
+    return elapsed * 1e3 / steps, avg
+
+
+def varlen_flops(lengths, Hq, d, causal):
+    """The dense convention per sequence: 4 Hq L^2 d, halved when causal."""
+    f = sum(4.0 * Hq * L * L * d * (0.5 if causal else 1.0) for L in lengths)
+    return f, 2.5 * f
+
+
+def varlen_cpu_baseline(x, lengths, Hq, Hkv, d, causal, budget_s):
+    """Oracle fwd+bwd of whole sequences of the packed batch (all heads), in
+    order until budget_s elapses; rate scaled by their algorithmic FLOPs."""
+    import numpy as np
+
+    from oracle import attention as ora
+    cores = host_cores()
+    cu = x["cu_seqlens"]
+    scale = 1.0 / math.sqrt(d)
+    done, n = 0.0, 0
+    with blas_threads(cores):
+        t0 = time.perf_counter()
+        for s in range(len(lengths)):
+            a, e = int(cu[s]), int(cu[s + 1])
+            one = np.array([0, e - a], np.int32)
+            sl = {k: x[k][a:e] for k in ("q", "k", "v", "do")}
+            ora.varlen_forward(sl["q"], sl["k"], sl["v"], one, scale, causal)
+            ora.varlen_backward(sl["q"], sl["k"], sl["v"], sl["do"], one, scale, causal)
+            f, b = varlen_flops([e - a], Hq, d, causal)
+            done += f + b
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+    return {"value": done / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {len(lengths)} sequences (all {Hq} heads) fwd+bwd in fp64, "
+                      f"{el:.1f} s; rate scaled by their algorithmic FLOPs"}
+
+
+def measure_varlen(fa, t, cu, lengths, Hq, Hkv, d, causal, det, steps, warmup):
+    import torch
+    T = sum(lengths)
+    scale = 1.0 / math.sqrt(d)
+    wsf = fa.varlen_fwd_workspace(len(lengths), T, Hq, Hkv, d, causal, "cuda")
+    wsb = fa.varlen_bwd_workspace(len(lengths), T, Hq, Hkv, d, causal, det, "cuda")
+
+    def step():
+        o, lse = fa.varlen_fwd(t["q"], t["k"], t["v"], cu, causal=causal, softmax_scale=scale,
+                               max_seqlen=max(lengths), workspace=wsf)
+        fa.varlen_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], cu, causal=causal,
+                      softmax_scale=scale, deterministic=det, max_seqlen=max(lengths),
+                      workspace=wsb)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    fa.timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = fa.timing_end()
+    if det:
+        assert fa.workspace_error(wsb) == 0
+    avg = {k: v[1] / max(1, v[0]) for k, v in kt.items()}
+    avg["bwd_total"] = sum(kt[k][1] for k in ("bwd_pre", "bwd_main", "bwd_post", "sched")) / max(
+        1, kt["bwd_main"][0])
+    avg["fwd_total"] = sum(kt[k][1] for k in ("fwd", "fwd_combine")) / max(1, kt["fwd"][0]) + \
+        avg["sched"]
+    return elapsed * 1e3 / steps, avg
+
+
+SWEEP_DENSE = [
+    # (config id, B, N, Hq, Hkv, d, causal)
+    ("C1", 4, 2048, 16, 16, 64, False), ("C1", 4, 2048, 16, 16, 64, True),
+    ("C1", 4, 2048, 16, 16, 128, False), ("C1", 4, 2048, 16, 16, 128, True),
+    ("H", 2, 8192, 16, 16, 128, True),
+    ("C2", 1, 16384, 16, 16, 128, True), ("C2", 1, 32768, 16, 16, 128, True),
+    ("C3", 2, 8192, 32, 4, 128, True), ("C3", 2, 8192, 32, 1, 128, True),
+]
+
+
+def sweep_line(cid, workload, value_flops, ms_step, avg, f_fwd, f_bwd, det, sched, cpu, extra):
+    fwd_ms = avg.get("fwd_total", avg["fwd"])
+    line = {
+        "sweep": cid, "workload": workload,
+        "dq_reduction": ("atomic", "semaphore-ordered", "partial-tile", "fused partial-tile")[det],
+        "tile_order": sched,
+        "value": value_flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "pct_of_peak": 100.0 * value_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "ms_per_step": ms_step,
+        "fwd_ms": fwd_ms, "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+        "fwd_pct_peak": 100.0 * f_fwd / (fwd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "bwd_ms": avg["bwd_total"], "bwd_main_ms": avg["bwd_main"],
+        "bwd_tflops": f_bwd / (avg["bwd_total"] * 1e-3) / 1e12,
+        "bwd_pct_peak": 100.0 * f_bwd / (avg["bwd_total"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    return line
+
+
+def run_sweep(args):
+    """One JSON line per workload of the scope table's measurement row: MHA 2K
+    (d = 64, 128; causal and not), the headline, long context 16K / 32K, GQA
+    / MQA, and the 65536-token packed batch; each in the fast (atomic) and the
+    deterministic (semaphore-ordered) mode, plus the headline and the packed
+    batch with the longest-first tile order switched off (FA_SCHED=natural)."""
+    import torch
+
+    from exact_attention_80_amd import fa, inputs
+    torch.cuda.set_device(0)
+    cpu_cache = {}
+    for cid, B, N, Hq, Hkv, d, causal in SWEEP_DENSE:
+        x = make_inputs(B, N, Hq, Hkv, d)
+        f_fwd, f_bwd = flops(B, N, Hq, d, causal)
+        key = (N, d, causal)
+        if key not in cpu_cache:
+            cpu_cache[key] = (cpu_baseline(B, N, Hq, Hkv, d, causal, args.cpu_budget)
+                              if args.cpu_budget > 0 else None)
+        scheds = ("longest-first", "natural") if cid == "H" else ("longest-first",)
+        for det in (0, 1):
+            for sched in scheds:
+                if sched == "natural":
+                    os.environ["FA_SCHED"] = "natural"
+                try:
+                    ms, avg = measure_dense(fa, x, B, N, Hq, Hkv, d, causal, det, args.steps,
+                                            args.warmup)
+                finally:
+                    os.environ.pop("FA_SCHED", None)
+                wl = (f"{'causal' if causal else 'non-causal'} B={B} Hq={Hq} Hkv={Hkv} N={N} "
+                      f"d={d}")
+                print(json.dumps(sweep_line(cid, wl, f_fwd + f_bwd, ms, avg, f_fwd, f_bwd, det,
+                                            sched, cpu_cache[key], {})), flush=True)
+        del x
+        torch.cuda.empty_cache()
+    # C4: the packed batch
+    lengths = inputs.varlen_lengths()
+    Hq = Hkv = 16
+    d = 128
+    xv = inputs.varlen_inputs(lengths, Hq, Hkv, d, seed=4)
+    t = {}
+    for n in ("q", "k", "v", "do"):
+        bits = inputs.bf16_bits(xv[n]).view("int16")
+        t[n] = torch.from_numpy(bits.copy()).to("cuda").view(torch.bfloat16)
+    cu = torch.from_numpy(xv["cu_seqlens"]).to("cuda")
+    f_fwd, f_bwd = varlen_flops(lengths, Hq, d, True)
+    cpu = (varlen_cpu_baseline(xv, lengths, Hq, Hkv, d, True, args.cpu_budget)
+           if args.cpu_budget > 0 else None)
+    for det in (0, 1):
+        for sched in ("longest-first", "natural"):
+            if sched == "natural":
+                os.environ["FA_SCHED"] = "natural"
+            try:
+                ms, avg = measure_varlen(fa, t, cu, lengths, Hq, Hkv, d, True, det, args.steps,
+                                         args.warmup)
+            finally:
+                os.environ.pop("FA_SCHED", None)
+            wl = (f"causal packed batch of {len(lengths)} sequences, {sum(lengths)} tokens "
+                  f"(log-uniform lengths 128..16384, longest {max(lengths)}), Hq=Hkv={Hq} d={d}")
+            print(json.dumps(sweep_line("C4", wl, f_fwd + f_bwd, ms, avg, f_fwd, f_bwd, det, sched,
+                                        cpu, {"lengths": lengths})), flush=True)
+
+
+def run_atomic_probe(args):
+    """What the fast backward's dQ reduction can sustain: its fp32 atomic adds
+    alone (same instructions, same 32 x 16 per-wave blocks of a [rows, Hq*d]
+    fp32 accumulator, 1024 workgroups), against plain stores of the same
+    bytes; the headline backward moves 2.21 GB this way per launch."""
+    import torch
+
+    from exact_attention_80_amd import fa
+    torch.cuda.set_device(0)
+    rows, row_floats = 2 * 8192, 16 * 128          # the headline's dQ accumulator
+    buf = torch.zeros((rows, row_floats), dtype=torch.float32, device="cuda")
+    blocks, items = 1024, 132                     # 1024 x 132 x 16 KiB = 2.21 GB
+    out = {"probe": "dq_reduction", "rows": rows, "row_floats": row_floats,
+           "blocks": blocks, "items": items}
+    launches = 0
+    for store in (False, True):
+        for _ in range(2):
+            fa.probe_dq_reduction(buf, blocks, items, store)
+        launches += 2
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        reps = 10
+        nbytes = 0
+        for _ in range(reps):
+            nbytes += fa.probe_dq_reduction(buf, blocks, items, store)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        launches += reps
+        key = "store" if store else "atomic"
+        out[f"{key}_ms"] = ms
+        out[f"{key}_tbps"] = nbytes / reps / (ms * 1e-3) / 1e12
+        out["bytes_per_launch"] = nbytes // reps
+        if not store:
+            # every atomic launch added 1/1024 to each element of the 4096-element
+            # tiles it visited (sums exact in fp32): all adds landed
+            want = launches * blocks * items * 4096 / 1024
+            got = float(buf.double().sum())
+            out["atomic_sum_check"] = got == want
+            if got != want:
+                raise RuntimeError(f"probe sum {got} != {want}")
+    print(json.dumps(out), flush=True)
+
+
+def device_info():
+    """CU count and clocks of the device (rocminfo), for the record."""
+    import subprocess
+    info = {}
+    try:
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60)
+        agent = None
+        for line in r.stdout.splitlines():
+            line = line.strip()
+            if line.startswith("Name:") and "gfx" in line:
+                agent = line.split(":", 1)[1].strip()
+                info["name"] = agent
+            if agent and line.startswith("Compute Unit:"):
+                info["compute_units"] = int(line.split(":", 1)[1])
+            if agent and line.startswith("Max Clock Freq. (MHz):"):
+                info["max_clock_mhz"] = int(line.split(":", 1)[1])
+            if agent and "compute_units" in info and "max_clock_mhz" in info:
+                break
+    except Exception as e:  # pragma: no cover
+        info["error"] = str(e)
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +627,14 @@ def main():
                          "forward with fp8 scores (extras)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per measured workload (MHA 2K, headline, 16K/32K, "
+                         "GQA/MQA, packed batch; atomic and ordered dQ; tile-order ablation)")
+    ap.add_argument("--atomic-probe", action="store_true",
+                    help="only measure the rate of the backward's dQ atomics and of plain "
+                         "stores of the same bytes")
+    ap.add_argument("--device-info", action="store_true",
+                    help="only print the device's CU count and clock (rocminfo)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -372,6 +652,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n}), flush=True)
+        return
+
+    if args.device_info:
+        print(json.dumps(device_info()), flush=True)
+        return
+    if args.atomic_probe:
+        run_atomic_probe(args)
+        return
+    if args.sweep:
+        run_sweep(args)
         return
 
     if args.workload == "decode":

@@ -2,6 +2,12 @@
 
 Every call recompiles all sources (in parallel) and relinks.  Objects go to
 exact_attention_80_amd/_build/, the library next to this file.
+
+Besides the library itself one variant is built for the tests:
+libfa_mi355x_tau0.so, whose forward rescales its accumulator on every growth
+of a row maximum (rescale threshold 0 instead of 8 log2 units).  Its results
+must agree with the default build's within rounding; the product never loads
+it.
 """
 
 from __future__ import annotations
@@ -18,12 +24,21 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_sched.hip"]
 
+# name -> (sources rebuilt for the variant, extra flags for them)
+VARIANTS = {
+    "tau0": (["fa_fwd.hip"], ["-DFA_RESCALE_TAU=0.0f"]),
+}
+
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(HERE, f"libfa_mi355x_{name}.so")
 
 
 def hipcc() -> str:
@@ -42,24 +57,40 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, jobs: int | None = None, extra_flags: list[str] | None = None) -> str:
-    """Compile all sources for gfx950 and link the library; returns its path."""
+def _link(cc, objs, path, verbose):
+    tmp = path + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, jobs: int | None = None, extra_flags: list[str] | None = None,
+          variants: bool = True) -> str:
+    """Compile all sources for gfx950 and link the library (and, unless
+    variants is False, the test variants); returns the library's path."""
     cc = hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     flags = HIP_FLAGS + list(extra_flags or [])
-    objs = []
+    objs = {}
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        objs.append(obj)
+        objs[src] = obj
         cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    var_objs = {}
+    if variants:
+        for name, (srcs, vflags) in VARIANTS.items():
+            var_objs[name] = dict(objs)
+            for src in srcs:
+                obj = os.path.join(BUILD_DIR, src.replace(".hip", f"_{name}.o"))
+                var_objs[name][src] = obj
+                cmds.append([cc, *flags, *vflags, "-c", os.path.join(CSRC, src), "-o", obj])
     workers = jobs or min(len(cmds), max(1, (os.cpu_count() or 2) // 2))
     with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
+    _link(cc, [objs[s] for s in SOURCES], LIB_PATH, verbose)
+    for name, vo in var_objs.items():
+        _link(cc, [vo[s] for s in SOURCES], variant_path(name), verbose)
     return LIB_PATH
 
 

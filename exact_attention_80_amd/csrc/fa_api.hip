@@ -80,7 +80,8 @@ int env_int(const char* name, int dflt) {
 }
 
 // Ablation switch for the tile order: FA_SCHED=natural disables longest-first
-// and XCD grouping (read on every call; results never depend on it).
+// and XCD grouping in the dense grids and the cost sort of the packed-batch
+// scheduler (read on every call; results never depend on it).
 int sched_mode() {
   const char* s = std::getenv("FA_SCHED");
   return (s && std::strcmp(s, "natural") == 0) ? 1 : 0;
@@ -151,6 +152,9 @@ int check_dims(long tokens, int Hq, int Hkv, int d, int causal, float scale) {
   if (tokens * (long)Hq * d >= (1L << 31) * 16L)
     return fail(FA_ERR_UNSUPPORTED, "tensor too large");
   if (tokens > (1L << 30)) return fail(FA_ERR_UNSUPPORTED, "too many tokens");
+  // per-tile buffer ranges (at most 64 rows of one token's heads, fp32 for the
+  // dQ accumulator) are 32-bit byte counts
+  if ((long)Hq * d >= (1L << 24)) return fail(FA_ERR_UNSUPPORTED, "Hq * d must be below 2^24");
   return FA_OK;
 }
 
@@ -335,7 +339,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bo
     const long tk = timing_start(4, s);
     int* split_base = reinterpret_cast<int*>(at(ws, lay.split_base));
     e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, br, 0, causal != 0, fa::fwd_tile_keys(),
-                         fa::kBwdBQ, tiles, lay.max_tiles, split_base, lay.max_split, hdr, s);
+                         fa::kBwdBQ, tiles, lay.max_tiles, split_base, lay.max_split, hdr,
+                         p.sched == 0, s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
@@ -445,7 +450,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, fa::bwd_tile_keys(d),
                          deterministic ? 2 : 1,
                          causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles,
-                         nullptr, 0, hdr, s);
+                         nullptr, 0, hdr, p.sched == 0, s);
     timing_stop(tk, s);
     if (e != hipSuccess) return hip_fail(e, "scheduler launch");
     p.cu_seqlens = cu;
@@ -644,6 +649,24 @@ int fa_varlen_qk_bwd(const void* q, const void* k, const void* v, const void* o,
   return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq,
                  total_q, total_k, Hq, Hkv, d, softmax_scale, causal, deterministic, ws, ws_bytes,
                  stream);
+}
+
+int fa_probe_dq_reduction(float* buf, int rows, int row_floats, int blocks, int items, int store,
+                          void* stream) {
+  int st;
+  if ((st = check_ptr(buf, "buf"))) return st;
+  if (rows <= 0 || rows % 32 != 0) return fail(FA_ERR_INVALID_ARG, "rows must be a positive multiple of 32");
+  if (row_floats <= 0 || row_floats % 128 != 0)
+    return fail(FA_ERR_INVALID_ARG, "row_floats must be a positive multiple of 128");
+  if ((long)row_floats * 32 * 4 >= (1L << 31)) return fail(FA_ERR_UNSUPPORTED, "rows too wide");
+  if (blocks <= 0 || items <= 0) return fail(FA_ERR_INVALID_ARG, "blocks and items must be positive");
+  if (store != 0 && store != 1) return fail(FA_ERR_INVALID_ARG, "store must be 0 or 1");
+  std::string why;
+  if ((st = check_device(&why))) return fail(st, why);
+  hipError_t e = fa::launch_probe_dq(buf, rows, row_floats, blocks, items, store != 0,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return FA_OK;
 }
 
 int fa_timing_begin(void) {

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
     const int h = h0 + hh;
     const int q0 = i * BQ;
     const long tok = (long)it.q_start + q0;
-    const uint32_t range = tile_range(q0, it.q_len, q_row * 2, D * 2);
+    const uint32_t range = tile_range(q0, it.q_len, q_row * 2, D * 2, BQ);
     qcopy.issue(qd, make_rsrc(p.q + tok * q_row + (long)h * D, range));
     qcopy.issue(dod, make_rsrc(p.dout + tok * q_row + (long)h * D, range));
     if (wave == NW - 1) {
@@ -868,7 +868,54 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* part, b
   }
 }
 
+// ---------------------------------------------------------------------------
+// Measurement aid: the atomic dQ reduction of bwd_kernel (d = 128) without
+// its products.  Workgroup w of 8 waves, at step t, takes the 32-row x 128-
+// column tile ((w + t * gridDim.x) mod tiles) of a [rows, row_floats] fp32
+// buffer; wave v adds its 32 x 16 column block with the 8 buffer atomic
+// instructions (4 rows x 16 columns each) the backward issues per item, or,
+// with STORE, writes the same bytes with plain stores.
+template <bool STORE>
+__global__ __launch_bounds__(512) void probe_dq_kernel(float* buf, int rows, int row_floats,
+                                                        int items) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int g16 = lane >> 4, L16 = lane & 15;
+  const int heads = row_floats / 128;
+  const long tiles = (long)(rows / 32) * heads;
+  const float val = 1.0f / 1024.0f;
+  for (int t = 0; t < items; ++t) {
+    const long tile = ((long)blockIdx.x + (long)t * gridDim.x) % tiles;
+    const int i = (int)(tile / heads), h = (int)(tile - (long)(tile / heads) * heads);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        buf + (long)i * 32 * row_floats + h * 128, (short)0, (31 * row_floats + 128) * 4,
+        0x00020000);
+    const int vo = ((4 * g16) * row_floats + wave * 16 + L16) * 4;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int off = vo + (16 * qb + r) * row_floats * 4;
+        if (STORE)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rsrc, off, 0, 0);
+        else
+          (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(val, rsrc, off, 0, 0);
+      }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_probe_dq(float* buf, int rows, int row_floats, int blocks, int items, bool store,
+                           hipStream_t stream) {
+  if (store)
+    hipLaunchKernelGGL(probe_dq_kernel<true>, dim3(blocks), dim3(512), 0, stream, buf, rows,
+                       row_floats, items);
+  else
+    hipLaunchKernelGGL(probe_dq_kernel<false>, dim3(blocks), dim3(512), 0, stream, buf, rows,
+                       row_floats, items);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int mode, int grid,
                       hipStream_t stream) {

@@ -256,10 +256,16 @@ __device__ __forceinline__ void dma4_buf(i32x4 rsrc, uint32_t voff, void* lds_wa
                :: "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
-// Byte range of a tile that starts at row `row0` of a sequence of `len` rows
-// of `row_bytes` pitch, `data_bytes` used per row (0 when the tile is empty).
-__device__ __forceinline__ uint32_t tile_range(int row0, int len, long row_bytes, int data_bytes) {
-  return row0 < len ? (uint32_t)((long)(len - 1 - row0) * row_bytes + data_bytes) : 0u;
+// Byte range of a tile of at most `tile_rows` rows that starts at row `row0`
+// of a sequence of `len` rows of `row_bytes` pitch, `data_bytes` used per row
+// (0 when the tile is empty).  The range ends with the tile's last valid row,
+// so it never spans more than tile_rows rows and fits in 32 bits whenever
+// tile_rows * row_bytes does (the host rejects shapes where it would not).
+__host__ __device__ __forceinline__ uint32_t tile_range(int row0, int len, long row_bytes,
+                                                        int data_bytes, int tile_rows) {
+  if (row0 >= len) return 0u;
+  const int rows = len - row0 < tile_rows ? len - row0 : tile_rows;
+  return (uint32_t)((long)(rows - 1) * row_bytes + data_bytes);
 }
 
 // Per-lane offsets of the uniform-count copy of one tile (see dma_count):

@@ -45,7 +45,13 @@ namespace fa {
 namespace {
 
 constexpr int kBC = 64;        // keys per K/V tile
-constexpr float kTau = 8.0f;   // rescale threshold (log2 units): p <= 2^8
+// Rescale threshold in log2 units (probabilities stay <= 2^kTau).  The
+// result does not depend on it; a build with FA_RESCALE_TAU=0 rescales on
+// every growth of a row maximum, which the tests compare against.
+#ifndef FA_RESCALE_TAU
+#define FA_RESCALE_TAU 8.0f
+#endif
+constexpr float kTau = FA_RESCALE_TAU;
 
 struct WorkItem {
   int seq_start;  // first query token of the sequence
@@ -216,9 +222,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     char* kt = kv_s[u % STAGES];
     const int j = jb + u;
     kcopy.issue(kt, make_rsrc(kbase + (long)j * kBC * k_bytes,
-                              tile_range(j * kBC, klen, k_bytes, D * EB)));
+                              tile_range(j * kBC, klen, k_bytes, D * EB, kBC)));
     vcopy.issue(kt + KT::kBytes, make_rsrc(vbase + (long)j * kBC * kv_row,
-                                           tile_range(j * kBC, klen, kv_bytes, D * 2)));
+                                           tile_range(j * kBC, klen, kv_bytes, D * 2, kBC)));
   };
 
   // ---- running softmax state (per lane = per query; both lane halves agree)

@@ -81,17 +81,23 @@ hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float s
                            const float* dk_part, const float* dv_part, bf16* dk, bf16* dv,
                            long kv_elems, int S, hipStream_t stream);
 
+// Measurement aid (fa_probe_dq_reduction): the backward's atomic dQ reduction
+// pattern alone, or the same bytes as plain stores.
+hipError_t launch_probe_dq(float* buf, int rows, int row_floats, int blocks, int items, bool store,
+                           hipStream_t stream);
+
 // Variable-length scheduler: validates the query and key offsets (cu_q and
 // cu_k may be the same array) and writes the ordered work list.
 //   mode 0: forward query tiles, longest first
 //   mode 1: backward key tiles, longest first
 //   mode 2: backward key tiles, deterministic order (key tiles of a sequence last-first)
+// With sorted == false the list keeps the natural order (sequence by sequence).
 // Mode 0 also writes split_base (nseq + 1 ints, first partial slot per
 // sequence) and flags an overflow when more than max_split chunks are needed.
 hipError_t launch_sched(const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k,
                         int tile, int mode, bool causal, int fwd_kv_tile, int bwd_q_tile,
                         int* tiles, int max_tiles, int* split_base, int max_split, uint32_t* hdr,
-                        hipStream_t stream);
+                        bool sorted, hipStream_t stream);
 
 // Forward combine of split tiles: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
 // per row, in ascending chunk order; one workgroup per (sequence, query head).

@@ -11,7 +11,8 @@
 //           which within a sequence is last key tile first ([FA4B] 3.3.1), so a
 //           key tile is always issued after every key tile it waits for.
 // The ordering only changes which work runs when, never any result.  Lists
-// longer than the in-LDS sort capacity are written in natural order (still
+// longer than the in-LDS sort capacity, or all lists when sorting is switched
+// off (the tile-order ablation), are written in natural order (still
 // last-tile-first within a sequence for mode 2).  Query and key offsets are
 // separate arrays (the same one when every sequence has Lq == Lk); forward
 // tiles split a sequence's queries, backward tiles its keys, and the cost of
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const 
                                                          int tile, int mode, int causal, int fkv,
                                                          int bq, int* tiles, int max_tiles,
                                                          int* split_base, int max_split,
-                                                         uint32_t* hdr) {
+                                                         uint32_t* hdr, int sorted) {
   __shared__ unsigned long long keys[kSortCap];
   __shared__ int scan[kThreads];
   __shared__ int scan2[kThreads];
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const 
     return;
   }
 
-  if (count <= kSortCap) {
+  if (sorted && count <= kSortCap) {
     int n = 1;
     while (n < count) n <<= 1;
     for (int s = s_lo; s < s_hi; ++s) {
@@ -254,10 +255,10 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const 
 hipError_t launch_sched(const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k,
                         int tile, int mode, bool causal, int fwd_kv_tile, int bwd_q_tile,
                         int* tiles, int max_tiles, int* split_base, int max_split, uint32_t* hdr,
-                        hipStream_t stream) {
+                        bool sorted, hipStream_t stream) {
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, cu_q, cu_k, nseq, total_q,
                      total_k, tile, mode, causal ? 1 : 0, fwd_kv_tile, bwd_q_tile, tiles,
-                     max_tiles, split_base, max_split, hdr);
+                     max_tiles, split_base, max_split, hdr, sorted ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -20,7 +20,6 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it first (python -m exact_attention_80_amd.build)")
 
-_lib = ctypes.CDLL(LIB_PATH)
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -46,13 +45,32 @@ _SIGS = {
     "fa_varlen_qk_bwd_workspace_size": ([_i] * 8, _sz),
     "fa_varlen_qk_bwd": ([_p] * 11 + [_i] * 8 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_workspace_error": ([_p, _sz, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
+    "fa_probe_dq_reduction": ([_p, _i, _i, _i, _i, _i, _p], _i),
     "fa_timing_begin": ([], _i),
     "fa_timing_end": ([ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)], _i),
 }
-for _name, (_args, _ret) in _SIGS.items():
-    _fn = getattr(_lib, _name)
-    _fn.argtypes = _args
-    _fn.restype = _ret
+
+
+def _load(path: str):
+    lib = ctypes.CDLL(path)
+    for name, (args, ret) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ret
+    return lib
+
+
+_lib = _load(LIB_PATH)
+
+
+def load_variant(name: str):
+    """The ctypes handle of a test variant built beside the library (see
+    build.VARIANTS), for the ``lib`` argument of fwd."""
+    from .build import variant_path
+    path = variant_path(name)
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it first (python -m exact_attention_80_amd.build)")
+    return _load(path)
 
 FA_OK = 0
 
@@ -99,8 +117,11 @@ def _scale(d, softmax_scale):
     return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
 
 
-def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None):
-    """Dense forward: q [B,N,Hq,d], k/v [B,N,Hkv,d] bf16 -> (o [B,N,Hq,d] bf16, lse [B,Hq,N] fp32)."""
+def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None, lib=None):
+    """Dense forward: q [B,N,Hq,d], k/v [B,N,Hkv,d] bf16 -> (o [B,N,Hq,d] bf16, lse [B,Hq,N] fp32).
+
+    lib: another build of the library (load_variant), default this package's."""
+    L = _lib if lib is None else lib
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     _need(q, "q", (B, N, Hq, d))
@@ -108,9 +129,9 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None):
     _need(v, "v", (B, N, Hkv, d))
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    ws_n = _lib.fa_fwd_workspace_size(B, N, Hq, Hkv, d, int(causal))
+    ws_n = L.fa_fwd_workspace_size(B, N, Hq, Hkv, d, int(causal))
     ws = _workspace(ws_n, q.device)
-    _check(_lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    _check(L.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
                        _ptr(ws), ws_n, _stream()), "fa_fwd")
     return o, lse
@@ -157,7 +178,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
     atomics, 1 (True) semaphore-ordered adds, 2 partial tiles summed in a fixed
     order by a second kernel, 3 partial tiles summed in a fixed order by the
     last workgroup to contribute to each query tile; 1, 2 and 3 are
-    bit-reproducible."""
+    bit-reproducible.  Mode 1 bounds its waits: one that expires leaves dQ
+    correct but unordered and sets a bit that workspace_error(workspace)
+    reports (check it after the call when reproducibility matters)."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     _need(q, "q", (B, N, Hq, d))
@@ -374,6 +397,16 @@ def timing_end() -> dict:
     ms = (ctypes.c_float * n)()
     _check(_lib.fa_timing_end(counts, ms), "fa_timing_end")
     return {k: (int(counts[i]), float(ms[i])) for i, k in enumerate(TIMING_KINDS)}
+
+
+def probe_dq_reduction(buf, blocks: int, items: int, store: bool = False) -> int:
+    """Launch the dQ-reduction measurement kernel on buf [rows, row_floats]
+    fp32 (rows % 32 == 0, row_floats % 128 == 0); returns the bytes it moves."""
+    _need(buf, "buf", tuple(buf.shape), torch.float32)
+    rows, row_floats = buf.shape
+    _check(_lib.fa_probe_dq_reduction(buf.data_ptr(), rows, row_floats, blocks, items, int(store),
+                                      _stream()), "fa_probe_dq_reduction")
+    return blocks * items * 16384
 
 
 def lib_path() -> str:

@@ -21,6 +21,10 @@ Recipe:
     query count is an integer drawn uniformly from [1, min(Lk, qmax)] (a
     chunk of new tokens); Q, dO are [Tq, Hq, d] and K, V [Tk, Hkv, d], drawn
     in the order Q, K, V, dO.
+  * wide score ranges (tests of the conditional rescale): the dense draws
+    with key j scaled by 1 + growth j / N before rounding (ramp_inputs); or
+    queries 1 + N(0, noise^2), the first 64 keys N(0, noise^2) and every later
+    key one constant level (plateau_inputs);
   * fp8 scores: the dense draws above before bf16 rounding; Q and K are each
     quantised per tensor to OCP e4m3 ("fn": largest finite 448, no
     infinities) with descale = amax(|x|) / 448 in float32 and bytes
@@ -70,6 +74,31 @@ def dense_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, seed: int = 0,
         a = g.standard_normal((B, N, h, d), dtype=np.float32)
         out[name] = bf16_round(a) if round_bf16 else a
     return out
+
+
+def ramp_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, seed: int = 0,
+                growth: float = 8.0) -> dict:
+    """The dense draws with key j multiplied by 1 + growth * j / N before the
+    bf16 rounding: key magnitudes grow along the sequence."""
+    x = dense_inputs(B, N, Hq, Hkv, d, seed=seed, round_bf16=False)
+    ramp = (1.0 + growth * np.arange(N, dtype=np.float32) / N)[None, :, None, None]
+    x["k"] = x["k"] * ramp
+    return {n: bf16_round(a) for n, a in x.items()}
+
+
+def plateau_inputs(N: int, Hq: int, Hkv: int, d: int, level: float, seed: int = 0,
+                   noise: float = 0.01, first: int = 64) -> dict:
+    """Dense inputs with B = 1: every query 1 + noise, the first `first` keys
+    pure noise, every later key equal to `level` in all components; noise
+    ~ N(0, noise^2); V and dO ~ N(0, 1).  Drawn in the order Q-noise,
+    K-noise, V, dO from Generator(PCG64(seed)), then bf16-rounded."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = 1.0 + noise * g.standard_normal((1, N, Hq, d), dtype=np.float32)
+    k = noise * g.standard_normal((1, N, Hkv, d), dtype=np.float32)
+    k[:, first:] = np.float32(level)
+    v = g.standard_normal((1, N, Hkv, d), dtype=np.float32)
+    do = g.standard_normal((1, N, Hq, d), dtype=np.float32)
+    return {"q": bf16_round(q), "k": bf16_round(k), "v": bf16_round(v), "do": bf16_round(do)}
 
 
 def varlen_lengths(total: int = 65536, lo: int = 128, hi: int = 16384, seed: int = 1) -> list[int]:

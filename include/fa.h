@@ -40,7 +40,8 @@
  *    word (fa_workspace_error), not by the return value.
  *  - d (head dimension) is 64, 128 or 256 (256: the fa_bwd partial-tile modes
  *    deterministic == 2, 3 are not offered; the fp8 forwards take 64 or 128).
- *    Hq must be a positive multiple of Hkv;
+ *    Hq must be a positive multiple of Hkv, and Hq * d below 2^24 (per-tile
+ *    buffer ranges are 32-bit; larger shapes return FA_ERR_UNSUPPORTED);
  *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
  *  - causal != 0 masks key j from query i when j > i ([FA2] "Core method" 2)
  *    when queries and keys have the same length.  The fa_varlen_qk_* calls
@@ -159,6 +160,14 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
  * Modes 1, 2 and 3 make dQ/dK/dV bit-identical from run to run (and the
  * partial-tile modes 2 and 3 give the same dQ).  dK/dV never use atomics.
  * Any other value: FA_ERR_INVALID_ARG.
+ * Mode 1 bounds every semaphore wait (2 s, or FA_DET_SPIN_TICKS ticks of the
+ * 100 MHz clock from the environment); a wait that expires sets
+ * FA_DEVERR_WAIT_TIMEOUT in the workspace and the adds proceed unordered, so
+ * the kernel always completes and dQ is still the correct sum, but not
+ * bit-reproducible.  The return value cannot report this (the call is
+ * asynchronous): a caller that relies on reproducibility must check
+ * fa_workspace_error() after the call (the same holds for fa_varlen_bwd and
+ * fa_varlen_qk_bwd with deterministic == 1).
  * Outputs dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] bf16.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -271,6 +280,19 @@ int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* 
  *           query tiles).
  * counts / ms must each point to FA_TIMING_KINDS elements (or be NULL).
  * Events are created lazily and reused; nothing is allocated on the device. */
+/* Measurement aid: the dQ reduction traffic of the fast backward (d = 128)
+ * without its products, to measure what the fp32 device atomics sustain
+ * ([FA4B] 2.1: dQ is reduced across key tiles by global atomic adds).
+ * `blocks` workgroups of 8 waves each take `items` 32-row x 128-column tiles
+ * of buf [rows, row_floats] fp32 (device memory, rows a multiple of 32,
+ * row_floats of 128) and add 1/1024 to every element of the tile with the
+ * backward's buffer atomic instructions (32 x 16 columns per wave, 4 rows x
+ * 16 columns per instruction), or, with store = 1, write the same bytes with
+ * plain stores.  Moves blocks * items * 16 KiB; asynchronous on `stream`;
+ * the caller times it. */
+int fa_probe_dq_reduction(float* buf, int rows, int row_floats, int blocks, int items, int store,
+                          void* stream);
+
 #define FA_TIMING_KINDS 6
 int fa_timing_begin(void);
 int fa_timing_end(int* counts, float* ms);

@@ -84,6 +84,8 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, N=128, Hq=2, Hkv=2, d=64, scale=0.1
     (dict(Hq=3, Hkv=2), INVALID), (dict(Hkv=0), INVALID), (dict(causal=2), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=512), UNSUPPORTED),
+    # per-tile byte ranges are 32-bit: one token's heads must stay below 2^24 elements
+    (dict(N=1, Hq=65536, Hkv=1, d=256), UNSUPPORTED),
 ])
 def test_fwd_rejects_bad_arguments(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -241,3 +243,4 @@ def test_varlen_qk_fwd_fp8_rejects_bad_arguments(lib):
     assert call(d=256) == UNSUPPORTED
     assert call(ws=None) == WORKSPACE
     assert call(nbytes=16) == WORKSPACE
+

@@ -318,3 +318,34 @@ def test_sampled_rows_and_keys_match_autograd(causal):
     gq, gk, gv = ora.attention_backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
     assert np.max(np.abs(dk_sum - gk[0, keys, 0])) <= 1e-12
     assert np.max(np.abs(dv_sum - gv[0, keys, 0])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_forward_backward_matches_autograd_and_batched_routines(causal):
+    """The whole-head routine (the reference of the full-size whole-head GPU
+    tests) against an independent torch float64 autograd, and against the
+    batched forward/backward on the same head: all five outputs, with rows
+    taken in chunks smaller than the head (three chunks and a ragged one)."""
+    pytest.importorskip("torch")
+    x = inputs.dense_inputs(1, 230, 2, 1, 32, seed=13, round_bf16=False)
+    scale = 0.21
+    o_b, lse_b = ora.attention_forward(x["q"], x["k"], x["v"], scale, causal)
+    dq_b, dk_b, dv_b = ora.attention_backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    dk_sum = np.zeros((230, 32))
+    dv_sum = np.zeros((230, 32))
+    for h in range(2):
+        args = (x["q"][0, :, h], x["k"][0, :, 0], x["v"][0, :, 0], x["do"][0, :, h])
+        got = ora.head_forward_backward(*args, scale, causal, row_chunk=64)
+        ref = _torch_reference(*(a.astype(np.float64) for a in args), scale, causal)
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
+            assert a.shape == b.shape, name
+            assert np.max(np.abs(a - b)) <= 1e-12, name
+        o, lse, dq, dk, dv = got
+        assert np.max(np.abs(o - o_b[0, :, h])) <= 1e-12
+        assert np.max(np.abs(lse - lse_b[0, h])) <= 1e-12
+        assert np.max(np.abs(dq - dq_b[0, :, h])) <= 1e-12
+        dk_sum += dk
+        dv_sum += dv
+    # the two query heads share key/value head 0: their dK, dV sum to the group's
+    assert np.max(np.abs(dk_sum - dk_b[0, :, 0])) <= 1e-12
+    assert np.max(np.abs(dv_sum - dv_b[0, :, 0])) <= 1e-12

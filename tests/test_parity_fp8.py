@@ -6,11 +6,17 @@ differences left are the kernel's accumulation and its bf16 P and O, as for
 the bf16 forward, and the same tolerances apply at the scale of these inputs.
 
 The fp8 matrix instruction does not round its 64-term sum like a chain of fp32
-additions: on the same operand values its score error is about 2^-16 of
-sum_d |q_d k_d| where the bf16 instruction's is about 2^-22.  For ordinary
-score ranges this stays far below the LSE tolerance; for the wide-range case
-below the LSE bound adds 2^-14 (four times the observed error) of
-scale * max_j sum_d |q_id k_jd| per query row."""
+additions: on the same operand values its score error was measured at about
+2^-16 of sum_d |q_d k_d|, where the bf16 instruction's is about 2^-22.  The
+LSE bar (1e-3) is therefore claimed for score ranges where
+scale * max_j sum_d |q_id k_jd| <= 32 (at most about 5e-4 of score error);
+the N(0, 1) draws of the ordinary cases stay near 12, the wide-range case
+checks on the CPU that its inputs stay inside it, and every case applies the
+plain bars.  The score error also moves O: by at most
+eps_i sum_j P_ij |V_jd - O_id| <= eps_i (sum_j P_ij |V_jd| + |O_id|), with
+eps_i the row's largest score error; the wide-range case adds that term to
+the O bound, with eps_i = 2^-15 scale max_j sum_d |q_id k_jd| (twice the
+measured rate of the instruction)."""
 
 import numpy as np
 import pytest
@@ -61,31 +67,49 @@ def test_fp8_forward_parity(fa, shape, causal):
     o, lse = fa.fwd_fp8(q8, bytes_to_dev(x["k8"]), to_dev(x["v"]), x["q_descale"],
                         x["k_descale"], causal=causal, softmax_scale=sc)
     ro, rlse = ora.attention_forward(x["q"], x["k"], x["v"], sc, causal)
-    errs = dict(o=max_abs(to_host(o), ro), o_excess=o_excess(to_host(o), ro),
+    pv, _ = ora.attention_forward(x["q"], x["k"], np.abs(x["v"]), sc, causal)
+    errs = dict(o=max_abs(to_host(o), ro), o_excess=o_excess(to_host(o), ro, pv, N),
                 lse=max_abs(to_host(lse), rlse))
     say(f"errors {errs}")
     assert errs["o_excess"] <= 1.0
     assert errs["lse"] <= TOL_LSE
 
 
+SCORE_RANGE = 32.0   # scale * max_j sum_d |q_id k_jd| up to which the LSE bar is claimed
+
+
+def score_magnitude(q, k, G, scale, causal):
+    """scale * max over visible keys of sum_d |q_id k_jd| per (head, row);
+    q [N, Hq, d], k [N, Hkv, d]."""
+    kk = np.repeat(k, G, axis=1)
+    mag = np.einsum("ihd,jhd->hij", np.abs(q), np.abs(kk)) * scale
+    if causal:
+        n = q.shape[0]
+        mag = np.where(np.tril(np.ones((n, n), dtype=bool)), mag, 0.0)
+    return mag.max(axis=2)
+
+
 def test_fp8_forward_wide_score_range(fa):
-    """Peaked softmax rows: descale factors that make |S| reach hundreds, so
-    the running maximum and the conditional rescale are exercised."""
+    """Descale factors 1.5 times the usual ones: scores up to about 11 in
+    natural-log units (16 in log2 units), the widest range inside SCORE_RANGE."""
     say("fp8 fwd wide scores B=1 N=500 Hq=4 Hkv=2 d=128")
     x = inputs.fp8_dense_inputs(1, 500, 4, 2, 128, seed=22)
-    qd, kd = x["q_descale"] * 8.0, x["k_descale"] * 8.0
+    f = 1.5
+    qd, kd = x["q_descale"] * f, x["k_descale"] * f
+    mag = score_magnitude(x["q"][0] * f, x["k"][0] * f, 2, scale_for(128), True)
+    say(f"scale * max sum |q||k| = {float(mag.max()):.1f}")
+    assert mag.max() <= SCORE_RANGE
     o, lse = fa.fwd_fp8(bytes_to_dev(x["q8"]), bytes_to_dev(x["k8"]), to_dev(x["v"]), qd, kd,
                         causal=True, softmax_scale=scale_for(128))
-    ro, rlse = ora.attention_forward(x["q"] * 8.0, x["k"] * 8.0, x["v"], scale_for(128), True)
-    assert o_excess(to_host(o), ro) <= 1.0
+    ro, rlse = ora.attention_forward(x["q"] * f, x["k"] * f, x["v"], scale_for(128), True)
+    pv, _ = ora.attention_forward(x["q"] * f, x["k"] * f, np.abs(x["v"]), scale_for(128), True)
     say(f"lse range {float(np.min(rlse)):.1f}..{float(np.max(rlse)):.1f}")
-    q, k = x["q"][0] * 8.0, x["k"][0] * 8.0                    # [N, H, d]
-    kk = np.repeat(k, 2, axis=1)                               # query head h uses key head h // 2
-    mag = np.einsum("ihd,jhd->hij", np.abs(q), np.abs(kk)) * scale_for(128)
-    mag = np.where(np.tril(np.ones((500, 500), dtype=bool)), mag, 0.0).max(axis=2)   # [H, N]
-    err = np.abs(to_host(lse)[0] - rlse[0])
-    say(f"lse err {float(err.max()):.2e}, bound from 2^-14 * max |q||k| up to {float(mag.max()) * 2.0 ** -14:.2e}")
-    assert np.all(err <= TOL_LSE + 2.0 ** -14 * mag)
+    # the instruction's score error moves O by at most eps_i (pv + |O*|)
+    eps = 2.0 ** -15 * mag.T[None, :, :, None]                   # [1, N, Hq, 1]
+    errs = dict(o_excess=o_excess(to_host(o), ro, pv, 500, extra=eps * (pv + np.abs(ro))),
+                lse=max_abs(to_host(lse), rlse))
+    say(f"errors {errs}")
+    assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE
 
 
 def test_fp8_forward_full_size(fa):
@@ -103,7 +127,8 @@ def test_fp8_forward_full_size(fa):
     b, h = 1, 7
     sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
     ro, rlse = ora.attention_forward(x["q"][sl], x["k"][sl], x["v"][sl], sc, True)
-    errs = dict(o_excess=o_excess(to_host(o[b:b + 1, :, h:h + 1]), ro),
+    pv, _ = ora.attention_forward(x["q"][sl], x["k"][sl], np.abs(x["v"][sl]), sc, True)
+    errs = dict(o_excess=o_excess(to_host(o[b:b + 1, :, h:h + 1]), ro, pv, N),
                 lse=max_abs(to_host(lse[b:b + 1, h:h + 1]), rlse))
     say(f"whole head b={b} h={h} errors {errs}")
     assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE
@@ -112,7 +137,8 @@ def test_fp8_forward_full_size(fa):
     for (b, h) in ((0, 0), (0, 15), (1, 3), (1, 12)):
         qh, kh, vh = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
         r_o, r_lse, _, _ = ora.head_query_rows(qh, kh, vh, np.zeros_like(vh), sc, True, rows)
-        e = dict(o_excess=o_excess(to_host(o[b, rows, h]), r_o),
+        pv = ora.head_query_rows(qh, kh, np.abs(vh), np.zeros_like(vh), sc, True, rows)[0]
+        e = dict(o_excess=o_excess(to_host(o[b, rows, h]), r_o, pv, N),
                  lse=max_abs(to_host(lse[b, h, rows]), r_lse))
         say(f"rows b={b} h={h} errors {e}")
         assert e["o_excess"] <= 1.0 and e["lse"] <= TOL_LSE
@@ -156,7 +182,9 @@ def test_fp8_varlen_qk_forward_parity(fa, case, causal):
     o, lse = to_host(o), to_host(lse)
     ro, rlse = ora.varlen_qk_forward(x["q"], x["k"], x["v"], x["cu_seqlens_q"],
                                      x["cu_seqlens_k"], sc, causal)
-    errs = dict(o_excess=o_excess(o, ro), lse=lse_error(lse, rlse))
+    pv, _ = ora.varlen_qk_forward(x["q"], x["k"], np.abs(x["v"]), x["cu_seqlens_q"],
+                                  x["cu_seqlens_k"], sc, causal)
+    errs = dict(o_excess=o_excess(o, ro, pv, max(lk)), lse=lse_error(lse, rlse))
     say(f"errors {errs}")
     assert np.all(np.isfinite(o))
     assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE

@@ -30,6 +30,7 @@ pytestmark = pytest.mark.gpu
 KEY_BLOCK = 512     # last keys of a sequence whose dK, dV are compared exactly
 ROW_SAMPLE = 96     # random query rows per head (plus the first and last 32)
 TOL_DV_SUM = 1e-2   # relative error of sum_j dV_j against sum_i dO_i
+TOL_DK_SUM = 1e-2   # |sum_j dK_j| relative to |sum_j |dK_j||
 
 
 @pytest.fixture(scope="module")
@@ -99,7 +100,10 @@ def check_whole_head(prob, grads, b, h, ref):
     """Every element of one query head (MHA: its dK, dV too) against the oracle."""
     dq, dk, dv = grads
     ro, rlse, rdq, rdk, rdv = ref
-    errs = dict(o=o_excess(host(prob.o[b, :, h]), ro),
+    q, k, v, _ = prob.head(b, h)
+    pv, _ = ora.attention_forward(q[None, :, None], k[None, :, None], np.abs(v)[None, :, None],
+                                  prob.scale, prob.causal)
+    errs = dict(o=o_excess(host(prob.o[b, :, h]), ro, pv[0, :, 0], prob.N),
                 lse=max_abs(host(prob.lse[b, h]), rlse),
                 dq=rel_fro(host(dq[b, :, h]), rdq))
     if prob.G == 1:
@@ -116,7 +120,8 @@ def check_rows(prob, grads, b, h, seed):
     rows = sample_rows(prob.N, seed)
     q, k, v, do = prob.head(b, h)
     ro, rlse, _, rdq = ora.head_query_rows(q, k, v, do, prob.scale, prob.causal, rows)
-    errs = dict(o=o_excess(host(prob.o[b, rows, h]), ro),
+    pv = ora.head_query_rows(q, k, np.abs(v), do, prob.scale, prob.causal, rows)[0]
+    errs = dict(o=o_excess(host(prob.o[b, rows, h]), ro, pv, prob.N),
                 lse=max_abs(host(prob.lse[b, h, rows]), rlse),
                 dq=rel_fro(host(grads[0][b, rows, h]), rdq))
     say(f"rows b={b} h={h} n={rows.size} errors {errs}")
@@ -137,6 +142,37 @@ def check_last_keys(prob, grads, b, g):
                 dv=rel_fro(host(grads[2][b, keys, g]), rdv))
     say(f"last keys b={b} g={g} errors {errs}")
     assert errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD
+
+
+def check_first_keys(prob, grads, b, g, nkeys=KEY_BLOCK):
+    """dK, dV of the FIRST nkeys keys of key/value head g (summed over its
+    group): every query row of the sequence contributes to them, so they carry
+    the longest accumulation chains of the backward."""
+    keys = np.arange(min(nkeys, prob.N))
+    rdk = np.zeros((keys.size, prob.d))
+    rdv = np.zeros((keys.size, prob.d))
+    for h in range(g * prob.G, (g + 1) * prob.G):
+        q, k, v, do = prob.head(b, h)
+        a, c = ora.head_key_rows(q, k, v, do, prob.scale, prob.causal, keys)
+        rdk += a
+        rdv += c
+    errs = dict(dk=rel_fro(host(grads[1][b, keys, g]), rdk),
+                dv=rel_fro(host(grads[2][b, keys, g]), rdv))
+    say(f"first keys b={b} g={g} errors {errs}")
+    assert errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD
+
+
+def check_dk_sum(dk_dev):
+    """Rows of dS sum to zero, so dK summed over the keys of a sequence is zero
+    for every batch entry and key/value head (dk [B,N,Hkv,d]).  Compared with
+    the sum of |dK_j|: random rounding leaves about 2^-9 / sqrt(N) of it, while
+    a dropped or misplaced block of query or key tiles leaves a share of the
+    order of that block's."""
+    s = dk_dev.float().sum(dim=1)
+    a = dk_dev.float().abs().sum(dim=1)
+    err = float(((s.norm(dim=-1) / a.norm(dim=-1).clamp_min(1e-30))).max())
+    say(f"sum_j dK_j vs sum_j |dK_j|: rel {err:.3e}")
+    assert err <= TOL_DK_SUM
 
 
 def check_dv_sum(dv_dev, do_dev, G):
@@ -170,6 +206,7 @@ def test_headline_whole_heads(headline, det):
     for (b, h), ref in refs.items():
         check_whole_head(prob, grads, b, h, ref)
     check_dv_sum(grads[2], prob.t["do"], 1)
+    check_dk_sum(grads[1])
 
 
 @pytest.mark.parametrize("mode", [1, 2, 3], ids=["ordered", "partial", "fused"])
@@ -194,6 +231,7 @@ def test_mha_2k(fa, d, causal):
         ref = ora.head_forward_backward(*prob.head(b, h), prob.scale, causal)
         check_whole_head(prob, grads, b, h, ref)
     check_dv_sum(grads[2], prob.t["do"], 1)
+    check_dk_sum(grads[1])
 
 
 # ---- head dimension 256: B=2 H=8 N=4096 causal -------------------------------------
@@ -208,6 +246,7 @@ def test_head_dim_256_whole_head(fa, det):
     check_rows(prob, grads, 0, 0, seed=1)
     check_last_keys(prob, grads, 0, 3)
     check_dv_sum(grads[2], prob.t["do"], 1)
+    check_dk_sum(grads[1])
 
 
 # ---- long context B=1 H=16 N=16384/32768 ----------------------------------------
@@ -220,7 +259,12 @@ def test_long_context(fa, N, det):
     for h in (0, 15):
         check_rows(prob, grads, 0, h, seed=h)
         check_last_keys(prob, grads, 0, h)
+    if N == 16384 and det == 0:
+        # the first keys: their dK, dV gather all 16384 query rows (512 query
+        # tiles, the longest chains of the backward)
+        check_first_keys(prob, grads, 0, 7)
     check_dv_sum(grads[2], prob.t["do"], 1)
+    check_dk_sum(grads[1])
 
 
 # ---- GQA / MQA B=2 Hq=32 Hkv=4/1 N=8192 ---------------------------------------------
@@ -235,6 +279,7 @@ def test_gqa_mqa(fa, hkv, det):
     check_last_keys(prob, grads, 0, 0)
     check_last_keys(prob, grads, 1, hkv - 1)
     check_dv_sum(grads[2], prob.t["do"], prob.G)
+    check_dk_sum(grads[1])
 
 
 # ---- packed batch of 65536 tokens, log-uniform lengths --------------------------------
@@ -275,9 +320,10 @@ def test_packed_varlen(fa, packed, det):
             q, k, v, do = (x[name][a:e, h] for name in ("q", "k", "v", "do"))
             rows = sample_rows(n, seed=1000 * s + h)
             ro, rlse, _, rdq = ora.head_query_rows(q, k, v, do, sc, True, rows)
+            pv = ora.head_query_rows(q, k, np.abs(v), do, sc, True, rows)[0]
             keys = np.arange(max(0, n - KEY_BLOCK // 2), n)
             rdk, rdv = ora.head_key_rows(q, k, v, do, sc, True, keys)
-            worst["o"] = max(worst["o"], o_excess(host(o[a + rows, h]), ro))
+            worst["o"] = max(worst["o"], o_excess(host(o[a + rows, h]), ro, pv, n))
             worst["lse"] = max(worst["lse"], max_abs(host(lse[h, a + rows]), rlse))
             worst["dq"] = max(worst["dq"], rel_fro(host(dq[a + rows, h]), rdq))
             worst["dk"] = max(worst["dk"], rel_fro(host(dk[a + keys, h]), rdk))
@@ -285,7 +331,33 @@ def test_packed_varlen(fa, packed, det):
         sdv = dv[a:e].float().sum(dim=0)
         sdo = t["do"][a:e].float().sum(dim=0)
         worst["dv_sum"] = max(worst["dv_sum"], float((sdv - sdo).norm() / sdo.norm()))
+        sdk = dk[a:e].float().sum(dim=0)
+        adk = dk[a:e].float().abs().sum(dim=0)
+        worst["dk_sum"] = max(worst.get("dk_sum", 0.0),
+                              float((sdk.norm(dim=-1) / adk.norm(dim=-1).clamp_min(1e-30)).max()))
     say(f"varlen worst errors {worst}")
     assert worst["o"] <= 1.0 and worst["lse"] <= TOL_LSE
     assert worst["dq"] <= TOL_GRAD and worst["dk"] <= TOL_GRAD and worst["dv"] <= TOL_GRAD
-    assert worst["dv_sum"] <= TOL_DV_SUM
+    assert worst["dv_sum"] <= TOL_DV_SUM and worst["dk_sum"] <= TOL_DK_SUM
+
+
+def test_packed_varlen_deterministic_bit_identical(fa, packed):
+    """The ordered dQ reduction of the packed batch (its own work order from
+    the scheduler, shortest first within each sequence) gives the same bits
+    on 10 repeated calls, with no device-reported error."""
+    import torch
+    x, t, cu, o, lse, sc = packed
+    ws = fa.varlen_bwd_workspace(cu.numel() - 1, x["q"].shape[0], 16, 16, 128, True, True,
+                                 "cuda")
+
+    def run():
+        g = fa.varlen_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], cu, causal=True,
+                          softmax_scale=sc, deterministic=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert fa.workspace_error(ws) == 0
+        return g
+
+    first = [a.clone() for a in run()]
+    for rep in range(10):
+        for a, b in zip(run(), first):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rep

@@ -68,7 +68,10 @@ def test_varlen_qk_parity(fa, case, causal, det):
                                      x["cu_seqlens_k"], sc, causal)
     rdq, rdk, rdv = ora.varlen_qk_backward(x["q"], x["k"], x["v"], x["do"], x["cu_seqlens_q"],
                                            x["cu_seqlens_k"], sc, causal)
-    errs = dict(o_excess=o_excess(o, ro), lse=lse_error(lse, rlse), dq=rel_fro(dq, rdq),
+    pv, _ = ora.varlen_qk_forward(x["q"], x["k"], np.abs(x["v"]), x["cu_seqlens_q"],
+                                  x["cu_seqlens_k"], sc, causal)
+    errs = dict(o_excess=o_excess(o, ro, pv, max(lk)), lse=lse_error(lse, rlse),
+                dq=rel_fro(dq, rdq),
                 dk=rel_fro(dk, rdk), dv=rel_fro(dv, rdv))
     say(f"errors {errs}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(dq))
@@ -98,7 +101,9 @@ def test_split_query_tiles(fa, case, causal):
     sc = scale_for(d)
     ro, rlse = ora.varlen_qk_forward(x["q"], x["k"], x["v"], x["cu_seqlens_q"],
                                      x["cu_seqlens_k"], sc, causal)
-    errs = dict(o_excess=o_excess(o, ro), lse=lse_error(lse, rlse))
+    pv, _ = ora.varlen_qk_forward(x["q"], x["k"], np.abs(x["v"]), x["cu_seqlens_q"],
+                                  x["cu_seqlens_k"], sc, causal)
+    errs = dict(o_excess=o_excess(o, ro, pv, max(lk)), lse=lse_error(lse, rlse))
     rdq, rdk, rdv = ora.varlen_qk_backward(x["q"], x["k"], x["v"], x["do"], x["cu_seqlens_q"],
                                            x["cu_seqlens_k"], sc, causal)
     dq, dk, dv = (to_host(a) for a in outs[2:])
@@ -121,8 +126,11 @@ def test_split_tiles_in_equal_length_batches(fa):
     o2, lse2 = fa.varlen_fwd(t["q"], t["k"], t["v"], cu, causal=True, softmax_scale=scale_for(128))
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
     ro, rlse = ora.varlen_forward(x["q"], x["k"], x["v"], x["cu_seqlens"], scale_for(128), True)
-    say(f"o_excess {o_excess(to_host(o), ro):.3f} lse {lse_error(to_host(lse), rlse):.2e}")
-    assert o_excess(to_host(o), ro) <= 1.0 and lse_error(to_host(lse), rlse) <= TOL_LSE
+    pv, _ = ora.varlen_forward(x["q"], x["k"], np.abs(x["v"]), x["cu_seqlens"], scale_for(128),
+                               True)
+    oe = o_excess(to_host(o), ro, pv, max(lengths))
+    say(f"o_excess {oe:.3f} lse {lse_error(to_host(lse), rlse):.2e}")
+    assert oe <= 1.0 and lse_error(to_host(lse), rlse) <= TOL_LSE
 
 
 def test_equal_lengths_match_the_single_offset_call(fa):
@@ -214,7 +222,8 @@ def test_decode_batch_full_size(fa, qk_problem, det):
         for h in range(g * G, (g + 1) * G):
             qh, doh = x["q"][qa:qe, h], x["do"][qa:qe, h]
             ro, rl, _, rdq = ora.head_query_rows(qh, kh, vh, doh, sc, True, rows, offset=off)
-            worst["o_excess"] = max(worst["o_excess"], o_excess(o[qa + rows, h], ro))
+            pv = ora.head_query_rows(qh, kh, np.abs(vh), doh, sc, True, rows, offset=off)[0]
+            worst["o_excess"] = max(worst["o_excess"], o_excess(o[qa + rows, h], ro, pv, ke - ka))
             worst["lse"] = max(worst["lse"], lse_error(lse[h, qa + rows], rl))
             worst["dq"] = max(worst["dq"], rel_fro(dq[qa + rows, h], rdq))
             a, b = ora.head_key_rows(qh, kh, vh, doh, sc, True, keys, offset=off)
