@@ -14,6 +14,9 @@
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
+// Scratch of fa_varlen_qk_fwd_noalloc (its size is FA_NOALLOC_SCRATCH_BYTES).
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using fa::BwdParams;
@@ -266,6 +269,35 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the no-allocation entry point: one static device array per GPU
+// (each device that loads the library holds its own copy).  Host code must
+// never use the array's name as a device address: its address on the current
+// device comes from hipGetSymbolAddress, looked up once per device.
+
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(FA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                  (e != hipSuccess ? hipGetErrorString(e) : "null address"));
+    it = g_scratch.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return FA_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -614,6 +646,34 @@ int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float
     return fail(FA_ERR_INVALID_ARG, "max_seqlen_q and max_seqlen_k must be >= 0");
   return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
                  Hq, Hkv, d, softmax_scale, causal, ws, ws_bytes, stream);
+}
+
+int fa_varlen_qk_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                             int Hq, int Hkv, int d, float softmax_scale, int causal,
+                             void* stream) {
+  if (nseq <= 0) return fail(FA_ERR_INVALID_ARG, "nseq must be positive");
+  if (max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q and max_seqlen_k must be >= 0");
+  // the argument checks of run_fwd, made before the scratch is looked up
+  int st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")) ||
+      (st = check_ptr(cu_seqlens_q, "cu_seqlens_q")) ||
+      (st = check_ptr(cu_seqlens_k, "cu_seqlens_k")))
+    return st;
+  if ((st = check_dims(total_q, Hq, Hkv, d, causal, softmax_scale))) return st;
+  if ((st = check_dims(total_k, Hq, Hkv, d, causal, softmax_scale))) return st;
+  const size_t need = fwd_layout(true, nseq, total_q, total_k, Hq, d).total;
+  if (need > kScratchBytes)
+    return fail(FA_ERR_WORKSPACE, "problem needs " + std::to_string(need) +
+                                      " bytes of scratch, more than the no-allocation limit of " +
+                                      std::to_string(kScratchBytes));
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return run_fwd(q, k, v, o, lse, true, 1, 0, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
+                 Hq, Hkv, d, softmax_scale, causal, ws, kScratchBytes, stream);
 }
 
 int fa_varlen_qk_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,

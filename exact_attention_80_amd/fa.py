@@ -42,6 +42,7 @@ _SIGS = {
     "fa_varlen_qk_fwd_workspace_size": ([_i] * 7, _sz),
     "fa_varlen_qk_fwd": ([_p] * 7 + [_i] * 8 + [_f, _i, _p, _sz, _p], _i),
     "fa_varlen_qk_fwd_fp8": ([_p] * 7 + [_i] * 8 + [_f, _f, _f, _i, _p, _sz, _p], _i),
+    "fa_varlen_qk_fwd_noalloc": ([_p] * 7 + [_i] * 8 + [_f, _i, _p], _i),
     "fa_varlen_qk_bwd_workspace_size": ([_i] * 8, _sz),
     "fa_varlen_qk_bwd": ([_p] * 11 + [_i] * 8 + [_f, _i, _i, _p, _sz, _p], _i),
     "fa_workspace_error": ([_p, _sz, _p, ctypes.POINTER(ctypes.c_uint32)], _i),
@@ -312,6 +313,40 @@ def varlen_qk_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
            "fa_varlen_qk_fwd")
     return o, lse
 
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_NOALLOC_SCRATCH_BYTES
+
+
+def varlen_qk_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
+                          softmax_scale: float | None = None, max_seqlen_q: int = 0,
+                          max_seqlen_k: int = 0, out=None):
+    """varlen_qk_fwd through the entry point that allocates nothing on the
+    device: the library's static per-GPU scratch array (NOALLOC_SCRATCH_BYTES)
+    replaces the workspace, and larger problems are rejected.  out=(o, lse)
+    writes into caller-provided tensors, so that nothing is allocated at all.
+    Calls that overlap in time on one GPU share the scratch and must not be
+    issued concurrently."""
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    _need(q, "q", (Tq, Hq, d))
+    _need(k, "k", (Tk, Hkv, d))
+    _need(v, "v", (Tk, Hkv, d))
+    nseq = _cu_pair(cu_seqlens_q, cu_seqlens_k)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", (Tq, Hq, d))
+        _need(lse, "lse", (Hq, Tq), torch.float32)
+    _check(_lib.fa_varlen_qk_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), cu_seqlens_q.data_ptr(),
+                                         cu_seqlens_k.data_ptr(), nseq, Tq, Tk,
+                                         int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
+                                         _scale(d, softmax_scale), int(causal), _stream()),
+           "fa_varlen_qk_fwd_noalloc")
+    return o, lse
 
 
 def varlen_qk_fwd_fp8(q8, k8, v, cu_seqlens_q, cu_seqlens_k, q_descale: float, k_descale: float,

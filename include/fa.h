@@ -232,6 +232,29 @@ int fa_varlen_qk_fwd(const void* q, const void* k, const void* v, void* o, float
                      int Hkv, int d, float softmax_scale, int causal, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid allocation): fa_varlen_qk_fwd
+ * with no workspace argument.  The same kernels use instead one scratch array
+ * of FA_NOALLOC_SCRATCH_BYTES per GPU, a static device array of the library
+ * that the GPU holds until the process ends; its address is looked up once
+ * per device on the first call there.  The caller still provides every input
+ * and output.  A problem whose workspace (fa_varlen_qk_fwd_workspace_size)
+ * exceeds FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_WORKSPACE before any
+ * launch.  Everything the kernels read from the scratch is written earlier
+ * in the same call (the error word and tile list by the scheduling kernel,
+ * the partial results of split tiles by the forward), so nothing carries
+ * over from one call to the next; but every call on a GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (on different streams or
+ * threads) race and must be serialised by the caller.  The device error word
+ * of this call is not readable through fa_workspace_error.  Allocates
+ * nothing, on the device or with any allocating library routine. */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fa_varlen_qk_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                             int Hq, int Hkv, int d, float softmax_scale, int causal,
+                             void* stream);
+
 /* fa_varlen_qk_fwd with fp8 scores, as in fa_fwd_fp8: q8 [total_q, Hq, d] and
  * k8 [total_k, Hkv, d] are OCP e4m3 bytes standing for q_descale * Q and
  * k_descale * K; v, o, lse, the offsets and the bottom-right causal mask as in

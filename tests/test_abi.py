@@ -38,6 +38,7 @@ def lib():
     L.fa_varlen_qk_fwd.argtypes = [p] * 7 + [i] * 8 + [f, i, p, sz, p]
     L.fa_varlen_qk_fwd_fp8.argtypes = [p] * 7 + [i] * 8 + [f, f, f, i, p, sz, p]
     L.fa_varlen_qk_bwd.argtypes = [p] * 11 + [i] * 8 + [f, i, i, p, sz, p]
+    L.fa_varlen_qk_fwd_noalloc.argtypes = [p] * 7 + [i] * 8 + [f, i, p]
     L.fa_varlen_qk_fwd_workspace_size.argtypes = [i] * 7
     L.fa_varlen_qk_fwd_workspace_size.restype = sz
     L.fa_varlen_qk_bwd_workspace_size.argtypes = [i] * 8
@@ -244,3 +245,24 @@ def test_varlen_qk_fwd_fp8_rejects_bad_arguments(lib):
     assert call(ws=None) == WORKSPACE
     assert call(nbytes=16) == WORKSPACE
 
+def test_noalloc_entry_point_checks_on_the_host(lib):
+    """fa_varlen_qk_fwd_noalloc rejects bad arguments and problems whose
+    workspace exceeds its static scratch (64 MiB) before touching the device."""
+    limit = 64 << 20
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+
+    def call(nseq=3, tq=30, tk=400, hq=2, hkv=2, d=64, cuq=P, q=P, maxk=0):
+        return lib.fa_varlen_qk_fwd_noalloc(q, P, P, P, P, cuq, P, nseq, tq, tk, 0, maxk, hq, hkv,
+                                            d, 0.1, 1, None)
+    assert call(nseq=0) == INVALID
+    assert call(maxk=-1) == INVALID
+    assert call(cuq=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(tk=0) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    # 400 sequences of 2048 keys, 64 heads of d = 256: the split-tile partials
+    # alone need far more than the scratch
+    assert lib.fa_varlen_qk_fwd_workspace_size(400, 400, 400 * 2048, 64, 8, 256, 1) > limit
+    assert call(nseq=400, tq=400, tk=400 * 2048, hq=64, hkv=8, d=256) == WORKSPACE
+    assert b"no-allocation limit" in lib.fa_last_error()
