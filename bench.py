@@ -18,12 +18,20 @@ Prints one JSON line.  Besides the headline it carries:
                 the recorded rocprofv3 counter runs (profiles/), or null when
                 the kernel sources changed since they were taken;
   extras        per-kernel times; in the atomic mode also the bytes of fp32 dQ
-                atomic adds per backward launch and the rate they imply
-                (device-scope fp32 atomics, not the matrix unit, bound that
-                kernel);
+                atomic adds per backward launch and the rate they imply, to
+                set beside what the atomics alone sustain (--atomic-probe):
+                that kernel has two co-bounds, its dQ atomic traffic and its
+                own compute path, both close to its measured time;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample (whole query
                 heads of the same workload) on this host's cores, scaled to the
                 metric's unit.
+
+Other modes: --sweep prints one line per measured workload (MHA 2K, the
+headline, long context 16K/32K, GQA/MQA, the 65536-token packed batch; fast and
+ordered dQ; with and without the longest-first tile order); --atomic-probe
+measures the backward's dQ atomic adds alone against plain stores of the same
+bytes; --device-info prints the CU count and clock; --workload decode times a
+packed batch with separate query and key lengths.
 """
 
 from __future__ import annotations
@@ -722,8 +730,9 @@ def main():
         "pct_of_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
     }
     if det == 0:
-        # the fast mode's dQ reduction: device-scope fp32 atomic adds, whose
-        # throughput (not the matrix unit) bounds the backward main kernel
+        # the fast mode's dQ reduction: device-scope fp32 atomic adds; the
+        # rate they imply over the kernel's time, against what they sustain
+        # alone (--atomic-probe), is one of the kernel's two co-bounds
         dq_bytes = dq_reduction_bytes(B, N, Hq, d, causal)
         extras["bwd_dq_atomic_bytes"] = dq_bytes
         extras["bwd_dq_atomic_tbps"] = dq_bytes / (avg_bwd_ms * 1e-3) / 1e12
