@@ -489,7 +489,10 @@ def run_sweep(args):
     from exact_attention_80_amd import fa, inputs
     torch.cuda.set_device(0)
     cpu_cache = {}
+    want = set(args.sweep_ids.split(",")) if args.sweep_ids else None
     for cid, B, N, Hq, Hkv, d, causal in SWEEP_DENSE:
+        if want is not None and cid not in want:
+            continue
         x = make_inputs(B, N, Hq, Hkv, d)
         f_fwd, f_bwd = flops(B, N, Hq, d, causal)
         key = (N, d, causal)
@@ -513,6 +516,8 @@ def run_sweep(args):
         del x
         torch.cuda.empty_cache()
     # C4: the packed batch
+    if want is not None and "C4" not in want:
+        return
     lengths = inputs.varlen_lengths()
     Hq = Hkv = 16
     d = 128
@@ -638,6 +643,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per measured workload (MHA 2K, headline, 16K/32K, "
                          "GQA/MQA, packed batch; atomic and ordered dQ; tile-order ablation)")
+    ap.add_argument("--sweep-ids", default="",
+                    help="with --sweep: only these workload ids, comma-separated "
+                         "(C1, H, C2, C3, C4)")
     ap.add_argument("--atomic-probe", action="store_true",
                     help="only measure the rate of the backward's dQ atomics and of plain "
                          "stores of the same bytes")

@@ -7,9 +7,14 @@
 // index map the attention kernel then follows).
 //   mode 0  forward query tiles, longest (most key tiles) first;
 //   mode 1  backward key tiles, longest (most query tiles) first;
-//   mode 2  backward key tiles for the deterministic reduction: cheapest first,
-//           which within a sequence is last key tile first ([FA4B] 3.3.1), so a
-//           key tile is always issued after every key tile it waits for.
+//   mode 2  backward key tiles for the deterministic reduction: sequences in
+//           descending order of their largest tile cost ([FA4B] 3.3.2 sorts
+//           the batches by per-tile time), the key tiles of a sequence kept
+//           together and last first ([FA4B] 3.3.1: the cheapest causal tiles
+//           first), so a key tile is always issued after every key tile it
+//           waits for.  (A global cheapest-first order ran the longest
+//           sequences' heaviest tiles last: 7.9 against 7.1 ms for the
+//           natural order on a 65536-token batch.)
 // The ordering only changes which work runs when, never any result.  Lists
 // longer than the in-LDS sort capacity, or all lists when sorting is switched
 // off (the tile-order ablation), are written in natural order (still
@@ -105,22 +110,21 @@ __device__ __forceinline__ int unkey_idx(int k) {
   return (k & (1 << 19)) ? (kSplitItem | (k & 0x7FFFF)) : k;
 }
 
+// ascending keys give: modes 0, 1 the most expensive item first; mode 2
+// (cost = the sequence's largest tile cost) the most expensive sequence
+// first, its key tiles together, last tile first
 __device__ __forceinline__ unsigned long long sort_key(int mode, int cost, int seq, int idx) {
-  const unsigned long long c = (unsigned long long)(unsigned)cost & 0xFFFFFFull;
+  const unsigned long long c = (unsigned long long)(unsigned)min(cost, 0xFFFFFF);
   const unsigned long long s = (unsigned long long)(unsigned)seq & 0xFFFFFull;
   const unsigned long long t = (unsigned long long)(unsigned)key_idx(idx) & 0xFFFFFull;
-  if (mode == 2) return (c << 40) | ((0xFFFFFull - t) << 20) | s;
+  if (mode == 2) return ((0xFFFFFFull - c) << 40) | (s << 20) | (0xFFFFFull - t);
   return ((0xFFFFFFull - c) << 40) | (s << 20) | t;
 }
 
 __device__ __forceinline__ void decode_key(int mode, unsigned long long k, int& seq, int& idx) {
-  if (mode == 2) {
-    seq = (int)(k & 0xFFFFFull);
-    idx = (int)(0xFFFFFull - ((k >> 20) & 0xFFFFFull));
-  } else {
-    idx = unkey_idx((int)(k & 0xFFFFFull));
-    seq = (int)((k >> 20) & 0xFFFFFull);
-  }
+  seq = (int)((k >> 20) & 0xFFFFFull);
+  if (mode == 2) idx = (int)(0xFFFFFull - (k & 0xFFFFFull));
+  else idx = unkey_idx((int)(k & 0xFFFFFull));
 }
 
 __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const int* cu_k,
@@ -204,10 +208,15 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const 
     for (int s = s_lo; s < s_hi; ++s) {
       const int lq = cu_q[s + 1] - cu_q[s], lk = cu_k[s + 1] - cu_k[s];
       const int nt = seq_items(mode, causal != 0, cu_q, cu_k, s, tile, fkv);
+      int seq_cost = 0;  // mode 2: the sequence's largest tile cost
+      if (mode == 2)
+        for (int k = 0; k < nt; ++k)
+          seq_cost = max(seq_cost, item_cost(mode, causal != 0, lq, lk, tile, k, fkv, bq));
       for (int k = 0; k < nt; ++k) {
         const int idx = seq_item_index(mode, causal != 0, lq, lk, tile, fkv, k);
-        keys[pos++] = sort_key(mode, item_cost(mode, causal != 0, lq, lk, tile, idx, fkv, bq), s,
-                               idx);
+        const int cost =
+            mode == 2 ? seq_cost : item_cost(mode, causal != 0, lq, lk, tile, idx, fkv, bq);
+        keys[pos++] = sort_key(mode, cost, s, idx);
       }
     }
     for (int x = count + tid; x < n; x += kThreads) keys[x] = ~0ull;
