@@ -786,6 +786,23 @@ def main():
             extras["fp8_fwd_pct_fp8_peak"] = 100.0 * extras["fp8_fwd_tflops"] / MFMA_FP8_PEAK_TFLOPS
             extras["fp8_fwd_speedup_vs_bf16"] = avg_fwd_ms / fp8_ms
             del q8, k8
+        # forward builds that differ in one compile-time choice: rescale at
+        # every growth of a row maximum (tau0), one exponential in four or two
+        # from the FMA-unit polynomial (exppoly4, exppoly2)
+        from exact_attention_80_amd.build import VARIANTS
+        for name in VARIANTS:
+            try:
+                lib = fa.load_variant(name)
+            except ImportError:
+                continue
+            for _ in range(3):
+                fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale, lib=lib)
+            torch.cuda.synchronize()
+            fa.timing_begin(lib)
+            for _ in range(args.steps):
+                fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale, lib=lib)
+            kv = fa.timing_end(lib)["fwd"]
+            extras[f"fwd_{name}_kernel_ms"] = kv[1] / max(1, kv[0])
 
     metric = METRIC
     if (B, N, Hq, Hkv, d, causal) != (2, 8192, 16, 16, 128, True):

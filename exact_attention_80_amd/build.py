@@ -27,6 +27,9 @@ SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_sched.hip"]
 # name -> (sources rebuilt for the variant, extra flags for them)
 VARIANTS = {
     "tau0": (["fa_fwd.hip"], ["-DFA_RESCALE_TAU=0.0f"]),
+    # one exponential in four (or two) from the FMA-unit polynomial
+    "exppoly4": (["fa_fwd.hip"], ["-DFA_EXP_POLY_EVERY=4"]),
+    "exppoly2": (["fa_fwd.hip"], ["-DFA_EXP_POLY_EVERY=2"]),
 }
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.

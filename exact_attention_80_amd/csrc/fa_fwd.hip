@@ -38,6 +38,7 @@
 //    the descale factors of Q and K are folded into the exponent scale c;
 //    P, V and the P V product stay bf16.
 #include "fa_common.h"
+#include "fa_exp2.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -52,6 +53,15 @@ constexpr int kBC = 64;        // keys per K/V tile
 #define FA_RESCALE_TAU 8.0f
 #endif
 constexpr float kTau = FA_RESCALE_TAU;
+// Exponentials on the FMA units: with FA_EXP_POLY_EVERY = k > 0, one
+// probability in k (register r of a lane's 16 with r % k == k - 1) comes
+// from poly_exp2 instead of the exponential instruction.  Off by default: on
+// this chip the instruction costs about two FMAs of issue time and the
+// polynomial eight, and the forward is not bound by its exponentials.
+#ifndef FA_EXP_POLY_EVERY
+#define FA_EXP_POLY_EVERY 0
+#endif
+constexpr int kPolyEvery = FA_EXP_POLY_EVERY;
 
 struct WorkItem {
   int seq_start;  // first query token of the sequence
@@ -335,7 +345,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(s[kb][r], p.c, -m_use));
+        const float x = fmaf(s[kb][r], p.c, -m_use);
+        const float pv = (kPolyEvery > 0 && r % kPolyEvery == kPolyEvery - 1) ? poly_exp2(x)
+                                                                               : fast_exp2(x);
         s[kb][r] = pv;
         lsum += pv;
       }

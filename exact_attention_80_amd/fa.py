@@ -77,16 +77,19 @@ FA_OK = 0
 
 
 class FAError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, lib=None):
         self.status = status
-        name = _lib.fa_status_string(status).decode()
-        detail = _lib.fa_last_error().decode()
+        L = _lib if lib is None else lib
+        name = L.fa_status_string(status).decode()
+        detail = L.fa_last_error().decode()
         super().__init__(f"{where}: {name}: {detail}")
 
 
-def _check(status: int, where: str) -> None:
+def _check(status: int, where: str, lib=None) -> None:
+    """Raise FAError for a failed call; lib is the library that was called
+    (its own last-error text), default this package's."""
     if status != FA_OK:
-        raise FAError(status, where)
+        raise FAError(status, where, lib)
 
 
 def _stream() -> int:
@@ -134,7 +137,7 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None, lib=N
     ws = _workspace(ws_n, q.device)
     _check(L.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
-                       _ptr(ws), ws_n, _stream()), "fa_fwd")
+                       _ptr(ws), ws_n, _stream()), "fa_fwd", L)
     return o, lse
 
 
@@ -289,11 +292,13 @@ def _cu_pair(cu_q, cu_k):
 
 def varlen_qk_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
                   softmax_scale: float | None = None, max_seqlen_q: int = 0,
-                  max_seqlen_k: int = 0, workspace: torch.Tensor | None = None):
+                  max_seqlen_k: int = 0, workspace: torch.Tensor | None = None, lib=None):
     """Packed forward with separate query and key lengths per sequence:
     q [Tq,Hq,d], k/v [Tk,Hkv,d], cu_seqlens_q / cu_seqlens_k int32 [nseq+1] on
     the device -> (o [Tq,Hq,d], lse [Hq,Tq]).  Causal masks are aligned
-    bottom-right (query i sees key j iff j <= i + Lk - Lq)."""
+    bottom-right (query i sees key j iff j <= i + Lk - Lq).  lib: another
+    build of the library (load_variant), default this package's."""
+    L = _lib if lib is None else lib
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
     _need(q, "q", (Tq, Hq, d))
@@ -304,13 +309,14 @@ def varlen_qk_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     ws = workspace
     if ws is None:
-        ws = varlen_qk_fwd_workspace(nseq, Tq, Tk, Hq, Hkv, d, causal, q.device)
-    _check(_lib.fa_varlen_qk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        ws = _workspace(L.fa_varlen_qk_fwd_workspace_size(nseq, Tq, Tk, Hq, Hkv, d, int(causal)),
+                        q.device)
+    _check(L.fa_varlen_qk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                  lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
                                  nseq, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
                                  _scale(d, softmax_scale), int(causal), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream()),
-           "fa_varlen_qk_fwd")
+           "fa_varlen_qk_fwd", L)
     return o, lse
 
 
@@ -420,17 +426,20 @@ def workspace_error(ws: torch.Tensor) -> int:
 TIMING_KINDS = ("fwd", "bwd_main", "bwd_pre", "bwd_post", "sched", "fwd_combine")
 
 
-def timing_begin() -> None:
-    """Start recording HIP events around every kernel this thread launches."""
-    _check(_lib.fa_timing_begin(), "fa_timing_begin")
+def timing_begin(lib=None) -> None:
+    """Start recording HIP events around every kernel this thread launches
+    (through lib, a variant from load_variant, or this package's library)."""
+    L = _lib if lib is None else lib
+    _check(L.fa_timing_begin(), "fa_timing_begin", L)
 
 
-def timing_end() -> dict:
+def timing_end(lib=None) -> dict:
     """Stop recording; returns {kind: (launches, total_ms)} for the kernels launched since."""
+    L = _lib if lib is None else lib
     n = len(TIMING_KINDS)
     counts = (ctypes.c_int * n)()
     ms = (ctypes.c_float * n)()
-    _check(_lib.fa_timing_end(counts, ms), "fa_timing_end")
+    _check(L.fa_timing_end(counts, ms), "fa_timing_end", L)
     return {k: (int(counts[i]), float(ms[i])) for i, k in enumerate(TIMING_KINDS)}
 
 

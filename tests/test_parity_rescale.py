@@ -135,7 +135,7 @@ def plateau_level(d, scale, lo, hi):
     """A bf16 key level whose score against an all-ones query lies between lo
     and hi log2 units (the bf16 grid there is about 0.03 to 0.05 units wide)."""
     t = np.float32((lo + hi) / 2 / (LOG2E * scale * d))
-    u = inputs.bf16_bits(inputs.bf16_round(t)).astype(np.int64)
+    u = int(np.asarray(inputs.bf16_bits(inputs.bf16_round(t))).reshape(-1)[0])
     for step in range(64):
         for cand in (u - step, u + step):
             level = float(inputs.bits_to_f32(np.array([cand], dtype=np.uint16))[0])
