@@ -640,6 +640,9 @@ def main():
                          "forward with fp8 scores (extras)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the forward of every build variant beside the library "
+                         "(extras fwd_<variant>_kernel_ms)")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per measured workload (MHA 2K, headline, 16K/32K, "
                          "GQA/MQA, packed batch; atomic and ordered dQ; tile-order ablation)")
@@ -786,6 +789,7 @@ def main():
             extras["fp8_fwd_pct_fp8_peak"] = 100.0 * extras["fp8_fwd_tflops"] / MFMA_FP8_PEAK_TFLOPS
             extras["fp8_fwd_speedup_vs_bf16"] = avg_fwd_ms / fp8_ms
             del q8, k8
+    if args.variants:
         # forward builds that differ in one compile-time choice: rescale at
         # every growth of a row maximum (tau0), one exponential in four or two
         # from the FMA-unit polynomial (exppoly4, exppoly2)
