@@ -33,6 +33,7 @@
 // forward kernel recomputes it (fwd_split_chunk_tiles).
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_sched_keys.h"
 
 namespace fa {
 
@@ -41,91 +42,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kSortCap = 8192;  // 64 KiB of 64-bit keys
 
-__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
-
-// chunks of sequence s's last query tile in the forward (0: not split)
-__device__ __forceinline__ int fwd_split_chunks(bool causal, int lq, int lk, int tile, int fkv) {
-  if (lq <= 0) return 0;
-  const int last = (lq - 1) / tile;
-  if (lq - last * tile > 32) return 0;
-  const int end = causal ? max(0, min(lk, (last + 1) * tile + lk - lq)) : lk;
-  const int nt = cdiv(end, fkv);
-  const int ct = fwd_split_chunk_tiles(nt);
-  const int n = cdiv(nt, ct);
-  return n >= 2 ? n : 0;
-}
-
-// cost of one tile in units of the inner loop's tiles
-__device__ __forceinline__ int tile_cost(int mode, bool causal, int lq, int lk, int tile, int idx,
-                                        int fkv, int bq) {
-  const int off = lk - lq;
-  if (mode == 0) {
-    const int end = causal ? max(0, min(lk, (idx + 1) * tile + off)) : lk;
-    return cdiv(end, fkv);
-  }
-  const int nq = cdiv(lq, bq);
-  return causal ? max(0, nq - max(0, idx * tile - off) / bq) : nq;
-}
-
-// cost of an item (a split chunk: its own key tiles)
-__device__ __forceinline__ int item_cost(int mode, bool causal, int lq, int lk, int tile, int idx,
-                                         int fkv, int bq) {
-  if (mode == 0 && (idx & kSplitItem)) {
-    const int last = (lq - 1) / tile;
-    const int end = causal ? max(0, min(lk, (last + 1) * tile + lk - lq)) : lk;
-    const int nt = cdiv(end, fkv);
-    const int ct = fwd_split_chunk_tiles(nt);
-    const int c = idx & 0xFFFFF;
-    return min(ct, nt - c * ct);
-  }
-  return tile_cost(mode, causal, lq, lk, tile, idx, fkv, bq);
-}
-
-// work items of sequence s: its query tiles (forward; a split last tile
-// counts once per chunk) or its key tiles (backward)
-__device__ __forceinline__ int seq_items(int mode, bool causal, const int* cu_q, const int* cu_k,
-                                         int s, int tile, int fkv) {
-  if (mode != 0) return cdiv(cu_k[s + 1] - cu_k[s], tile);
-  const int lq = cu_q[s + 1] - cu_q[s], lk = cu_k[s + 1] - cu_k[s];
-  const int n = fwd_split_chunks(causal, lq, lk, tile, fkv);
-  return cdiv(lq, tile) + (n > 0 ? n - 1 : 0);
-}
-
-// item k (0-based, in natural order) of sequence s: its tile index, or for a
-// chunk of a split forward tile kSplitItem | chunk
-__device__ __forceinline__ int seq_item_index(int mode, bool causal, int lq, int lk, int tile,
-                                              int fkv, int k) {
-  if (mode != 0) return k;
-  const int n = fwd_split_chunks(causal, lq, lk, tile, fkv);
-  const int nq = cdiv(lq, tile);
-  if (n == 0 || k < nq - 1) return k;
-  return kSplitItem | (k - (nq - 1));
-}
-
-// sort keys hold an item index in 20 bits: a split chunk is bit 19 | chunk
-__device__ __forceinline__ int key_idx(int idx) {
-  return (idx & kSplitItem) ? ((1 << 19) | (idx & 0x7FFFF)) : idx;
-}
-__device__ __forceinline__ int unkey_idx(int k) {
-  return (k & (1 << 19)) ? (kSplitItem | (k & 0x7FFFF)) : k;
-}
-
-// ascending keys give: modes 0, 1 the most expensive item first; mode 2
-// (cost = the sequence's largest tile cost) the most expensive sequence
-// first, its key tiles together, last tile first
-__device__ __forceinline__ unsigned long long sort_key(int mode, int cost, int seq, int idx) {
-  const unsigned long long c = (unsigned long long)(unsigned)min(cost, 0xFFFFFF);
-  const unsigned long long s = (unsigned long long)(unsigned)seq & 0xFFFFFull;
-  const unsigned long long t = (unsigned long long)(unsigned)key_idx(idx) & 0xFFFFFull;
-  if (mode == 2) return ((0xFFFFFFull - c) << 40) | (s << 20) | (0xFFFFFull - t);
-  return ((0xFFFFFFull - c) << 40) | (s << 20) | t;
-}
-
-__device__ __forceinline__ void decode_key(int mode, unsigned long long k, int& seq, int& idx) {
-  seq = (int)((k >> 20) & 0xFFFFFull);
-  if (mode == 2) idx = (int)(0xFFFFFull - (k & 0xFFFFFull));
-  else idx = unkey_idx((int)(k & 0xFFFFFull));
-}
+using namespace sched;
 
 __global__ __launch_bounds__(kThreads) void sched_kernel(const int* cu_q, const int* cu_k,
                                                          int nseq, int total_q, int total_k,
