@@ -142,9 +142,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using VT = SwzTile<kBC, CH, D == 256 ? 36 : (D == 128 ? 20 : 12)>;
 
   constexpr int STAGES = fwd_stages(D);          // K/V tiles in flight or in use
-  // bf16 operands of a tile's products are read in bulk ahead of them (the
-  // d = 256 and fp8 variants keep the interleaved reads)
-  constexpr bool PREFETCH = !FP8 && D <= 128;
+  // the K (bf16 or fp8) operands of a tile's products and its first V^T
+  // operands are read in bulk ahead of them (d = 256 keeps interleaved reads)
+  constexpr bool PREFETCH = D <= 128;
+  static_assert(!FP8 || D <= 128, "fp8 scores take d = 64 or 128");
   __shared__ __attribute__((aligned(16))) char kv_s[STAGES][KT::kBytes + VT::kBytes];
 
   WorkItem wi = fwd_work_item<CAUSAL, VARLEN>(p);
@@ -258,17 +259,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
     if (FP8) {
+      // every fp8 K operand of the tile is read before the first product
+      i32x8 kf8[D / 64][2];
 #pragma unroll
-      for (int dc = 0; dc < D / 64; ++dc) {
+      for (int dc = 0; dc < D / 64; ++dc)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const char* src = kt + (kb * 32 + l32) * KT::kPitch + 64 * dc + 32 * half;
           const u32x4 a0 = ld_lds16(src), a1 = ld_lds16(src + 16);
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          s[kb] = mfma32x32x64_fp8(a, qf8[dc], s[kb]);
+          kf8[dc][kb] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
         }
-      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dc = 0; dc < D / 64; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x64_fp8(kf8[dc][kb], qf8[dc], s[kb]);
     } else if (PREFETCH) {
       // every K operand of the tile is read before the first product, so the
       // products wait on one LDS latency instead of one per product pair

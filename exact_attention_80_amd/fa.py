@@ -150,10 +150,12 @@ def _e4m3_bytes(t, name, shape):
 
 
 def fwd_fp8(q8, k8, v, q_descale: float, k_descale: float, causal: bool = False,
-            softmax_scale: float | None = None):
+            softmax_scale: float | None = None, lib=None):
     """Dense forward with fp8 scores: q8 [B,N,Hq,d], k8 [B,N,Hkv,d] OCP e4m3 bytes
     (uint8 or float8_e4m3fn) standing for q_descale * q8 and k_descale * k8, v
-    [B,N,Hkv,d] bf16 -> (o [B,N,Hq,d] bf16, lse [B,Hq,N] fp32).  d = 64 or 128."""
+    [B,N,Hkv,d] bf16 -> (o [B,N,Hq,d] bf16, lse [B,Hq,N] fp32).  d = 64 or 128.
+    lib: another build of the library (load_variant), default this package's."""
+    L = _lib if lib is None else lib
     B, N, Hq, d = q8.shape
     Hkv = k8.shape[2]
     q8 = _e4m3_bytes(q8, "q8", (B, N, Hq, d))
@@ -161,10 +163,10 @@ def fwd_fp8(q8, k8, v, q_descale: float, k_descale: float, causal: bool = False,
     _need(v, "v", (B, N, Hkv, d))
     o = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=v.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=v.device)
-    _check(_lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
-                           lse.data_ptr(), B, N, Hq, Hkv, d, _scale(d, softmax_scale),
-                           float(q_descale), float(k_descale), int(causal), _stream()),
-           "fa_fwd_fp8")
+    _check(L.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr(), B, N, Hq, Hkv, d, _scale(d, softmax_scale),
+                        float(q_descale), float(k_descale), int(causal), _stream()),
+           "fa_fwd_fp8", L)
     return o, lse
 
 
