@@ -177,7 +177,7 @@ def bwd_workspace(q, k, causal: bool, deterministic: int | bool) -> torch.Tensor
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None = None,
-        deterministic: int | bool = False, workspace: torch.Tensor | None = None):
+        deterministic: int | bool = False, workspace: torch.Tensor | None = None, lib=None):
     """Dense backward -> (dq [B,N,Hq,d], dk [B,N,Hkv,d], dv [B,N,Hkv,d]) bf16.
 
     deterministic selects the dQ reduction across key tiles: 0 (False) fp32
@@ -186,7 +186,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
     last workgroup to contribute to each query tile; 1, 2 and 3 are
     bit-reproducible.  Mode 1 bounds its waits: one that expires leaves dQ
     correct but unordered and sets a bit that workspace_error(workspace)
-    reports (check it after the call when reproducibility matters)."""
+    reports (check it after the call when reproducibility matters).  lib:
+    another build of the library (load_variant), default this package's."""
+    L = _lib if lib is None else lib
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     _need(q, "q", (B, N, Hq, d))
@@ -198,11 +200,15 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ws = bwd_workspace(q, k, causal, deterministic) if workspace is None else workspace
-    _check(_lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal), int(deterministic),
-                       ws.data_ptr(), ws.numel(), _stream()), "fa_bwd")
+    if workspace is None:
+        n = L.fa_bwd_workspace_size(B, N, Hq, Hkv, d, int(causal), int(deterministic))
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    else:
+        ws = workspace
+    _check(L.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    B, N, Hq, Hkv, d, _scale(d, softmax_scale), int(causal), int(deterministic),
+                    ws.data_ptr(), ws.numel(), _stream()), "fa_bwd", L)
     return dq, dk, dv
 
 
