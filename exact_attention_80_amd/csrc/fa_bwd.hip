@@ -220,12 +220,13 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   const int nsteps = max(0, it.nq - i_start);
   const int nitems = GS * nsteps;
   // query tile of step u of a head's walk.  Causal, every mode but the
-  // ordered one: from the last query tile down to the diagonal, so the key
-  // tiles of a head read the same Q / dO tile at about the same step (they
-  // share it in L2, and in the fused mode the last-contributor sums spread
-  // over the workgroups).  The ordered mode walks from the diagonal upwards:
-  // a dQ tile's writers apply in descending key-tile order, and a top-down
-  // walk would make every key tile's first step wait for all higher ones.
+  // ordered one: from the last query tile down to the diagonal (measured
+  // faster than the upward walk in the atomic and partial-tile modes; in the
+  // fused mode the key tiles then reach a query tile at about the same step,
+  // which spreads the last-contributor sums over the workgroups).  The
+  // ordered mode walks from the diagonal upwards: a dQ tile's writers apply
+  // in descending key-tile order, and a top-down walk would make every key
+  // tile's first step wait for all higher ones.
   auto step_tile = [&](int u) { return (!DET && CAUSAL) ? it.nq - 1 - u : i_start + u; };
 
   // direct copy of one query tile's Q, dO rows (rows past the sequence end
