@@ -25,6 +25,11 @@ Recipe:
     with key j scaled by 1 + growth j / N before rounding (ramp_inputs); or
     queries 1 + N(0, noise^2), the first 64 keys N(0, noise^2) and every later
     key one constant level (plateau_inputs);
+  * tensors too large to draw on the host in seconds (tests of sizes past
+    4 GiB per tensor): torch's counter-based Philox generator on the device,
+    seeded per tensor (device_normal_bf16), standard-normal float32 rounded
+    to bf16 by torch (nearest, ties to even); the oracle side copies back the
+    slices it needs;
   * fp8 scores: the dense draws above before bf16 rounding; Q and K are each
     quantised per tensor to OCP e4m3 ("fn": largest finite 448, no
     infinities) with descale = amax(|x|) / 448 in float32 and bytes
@@ -48,6 +53,15 @@ def bf16_round(x) -> np.ndarray:
     out = r.astype(np.uint32).view(np.float32).copy()
     out[nan] = np.nan
     return out
+
+
+def device_normal_bf16(shape, seed: int, device: str = "cuda"):
+    """A standard-normal tensor drawn on the device by torch's Philox
+    generator seeded with `seed`, rounded to bf16 (nearest, ties to even)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
 
 
 def bf16_bits(x) -> np.ndarray:
