@@ -9,7 +9,9 @@ token's row is 32 KiB, a tensor 4.3 GB.  The inputs are drawn on the device
 against the fp64 oracle, as in the other full-size tests: sampled query rows
 (the first and last 32 plus random ones) of the first and last head (O, LSE,
 dQ), the dK, dV of the last 256 keys of those heads, and for both heads the
-size-independent identities sum_j dV_j = sum_i dO_i and sum_j dK_j = 0.
+size-independent identities sum_j dV_j = sum_i dO_i and sum_j dK_j = 0; and
+the same tensors as a packed batch of two sequences, checked the same way on
+the second one.
 """
 
 import numpy as np
@@ -73,3 +75,35 @@ def test_rows_keys_and_identities_past_4gib(problem, h):
     assert errs["o"] <= 1.0 and errs["lse"] <= TOL_LSE and errs["dq"] <= TOL_GRAD
     assert errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD
     assert errs["sum_dv"] <= TOL_SUM and errs["sum_dk"] <= TOL_SUM
+
+
+def test_packed_batch_past_4gib(problem):
+    """The same tensors as a packed batch [T, H, d] of two sequences (1000 and
+    N - 1000 tokens): the second sequence's late rows and last keys, which
+    lie past 2^32 bytes, against the oracle on that sequence alone."""
+    import torch
+    from exact_attention_80_amd import fa
+    t, _, _, _, sc = problem
+    first = 1000
+    cu = torch.tensor([0, first, N], dtype=torch.int32, device="cuda")
+    pk = {n: t[n][0] for n in ("q", "k", "v", "do")}
+    o, lse = fa.varlen_fwd(pk["q"], pk["k"], pk["v"], cu, causal=True, softmax_scale=sc)
+    dq, dk, dv = fa.varlen_bwd(pk["q"], pk["k"], pk["v"], o, lse, pk["do"], cu, causal=True,
+                               softmax_scale=sc)
+    torch.cuda.synchronize()
+    h = 77
+    L = N - first
+    rng = np.random.Generator(np.random.PCG64(72))
+    rows = np.unique(np.r_[np.arange(L - 32, L), rng.integers(0, L, 32)])
+    qh, kh, vh, doh = (host(pk[n][first:, h]) for n in ("q", "k", "v", "do"))
+    ro, rlse, _, rdq = ora.head_query_rows(qh, kh, vh, doh, sc, True, rows)
+    pv = ora.head_query_rows(qh, kh, np.abs(vh), doh, sc, True, rows)[0]
+    keys = np.arange(L - KEYS, L)
+    rdk, rdv = ora.head_key_rows(qh, kh, vh, doh, sc, True, keys)
+    errs = dict(o=o_excess(host(o[first + rows, h]), ro, pv, L),
+                lse=max_abs(host(lse[h, first + rows]), rlse),
+                dq=rel_fro(host(dq[first + rows, h]), rdq),
+                dk=rel_fro(host(dk[N - KEYS:, h]), rdk), dv=rel_fro(host(dv[N - KEYS:, h]), rdv))
+    say(f"packed h={h} rows={rows.size} errors {errs}")
+    assert errs["o"] <= 1.0 and errs["lse"] <= TOL_LSE and errs["dq"] <= TOL_GRAD
+    assert errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD
