@@ -8,7 +8,7 @@
 //    key/value tile, so no reduction between waves is ever needed;
 //  * K and V tiles of 64 keys are copied global->LDS by direct loads (no
 //    register staging) into padded tiles, through a ring of fwd_stages(D)
-//    buffers (4; 2 for d = 256, whose workgroups have 4 waves): the next
+//    buffers (4; 2 for d = 256, whose tiles are twice as large): the next
 //    tiles are in flight while tile j is computed; with 8 waves the first
 //    four issue all copies, after their own products of a tile (they run
 //    ahead of their SIMD partners, which are the critical path);
@@ -552,11 +552,10 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool varlen, int g
                       hipStream_t stream) {
   constexpr int NW = kFwdWaves;
   if (d == 256) {
-    constexpr int NW4 = fwd_waves(256);
-    if (causal) return varlen ? launch_fwd_t<256, NW4, true, true>(p, grid, stream)
-                              : launch_fwd_t<256, NW4, true, false>(p, grid, stream);
-    return varlen ? launch_fwd_t<256, NW4, false, true>(p, grid, stream)
-                  : launch_fwd_t<256, NW4, false, false>(p, grid, stream);
+    if (causal) return varlen ? launch_fwd_t<256, NW, true, true>(p, grid, stream)
+                              : launch_fwd_t<256, NW, true, false>(p, grid, stream);
+    return varlen ? launch_fwd_t<256, NW, false, true>(p, grid, stream)
+                  : launch_fwd_t<256, NW, false, false>(p, grid, stream);
   }
   if (d == 128) {
     if (causal) return varlen ? launch_fwd_t<128, NW, true, true>(p, grid, stream)

@@ -78,12 +78,13 @@ def test_dense_parity(fa, shape, causal):
 
 
 HEAD256_CASES = [
-    # d = 256: 4-wave workgroups (128 query rows / 128 keys); ragged tails,
-    # GQA/MQA, a single token
+    # d = 256: 256-row forward tiles, 128-key backward workgroups; ragged
+    # tails on both, GQA/MQA, a single token
     (1, 300, 2, 1, 256),
     (2, 129, 4, 4, 256),
     (1, 1, 2, 2, 256),
     (1, 513, 4, 2, 256),
+    (1, 257, 2, 2, 256),
 ]
 
 

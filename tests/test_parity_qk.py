@@ -88,7 +88,7 @@ SPLIT_CASES = [
     # into chunks of 32 key tiles and merged by the combine kernel
     ([1, 17, 32, 33, 257, 288, 289], [5000, 5000, 2049, 5000, 3000, 2100, 2100], 4, 2, 128),
     ([1, 3], [70000, 4100], 2, 1, 64),
-    ([1, 129, 160], [4500, 3000, 2100], 2, 2, 256),
+    ([1, 257, 288], [4500, 3000, 2100], 2, 2, 256),
 ]
 
 
