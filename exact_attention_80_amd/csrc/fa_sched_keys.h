@@ -82,21 +82,23 @@ __host__ __device__ __forceinline__ int unkey_idx(int k) {
   return (k & (1 << 19)) ? (kSplitItem | (k & 0x7FFFF)) : k;
 }
 
-// ascending keys give: modes 0, 1 the most expensive item first; mode 2
-// (cost = the sequence's largest tile cost) the most expensive sequence
-// first, its key tiles together, last tile first
+// ascending keys give: modes 0 and 2 (cost = the sequence's largest tile
+// cost) the sequences in descending order of it, each sequence's items
+// together, mode 0 from the last query tile (split chunks first), mode 2
+// from the last key tile; mode 1 (cost = the tile's own) every key tile in
+// descending order of its cost
 __host__ __device__ __forceinline__ unsigned long long sort_key(int mode, int cost, int seq, int idx) {
   const unsigned long long c = (unsigned long long)(unsigned)imin(cost, 0xFFFFFF);
   const unsigned long long s = (unsigned long long)(unsigned)seq & 0xFFFFFull;
   const unsigned long long t = (unsigned long long)(unsigned)key_idx(idx) & 0xFFFFFull;
-  if (mode == 2) return ((0xFFFFFFull - c) << 40) | (s << 20) | (0xFFFFFull - t);
-  return ((0xFFFFFFull - c) << 40) | (s << 20) | t;
+  if (mode == 1) return ((0xFFFFFFull - c) << 40) | (s << 20) | t;
+  return ((0xFFFFFFull - c) << 40) | (s << 20) | (0xFFFFFull - t);
 }
 
 __host__ __device__ __forceinline__ void decode_key(int mode, unsigned long long k, int& seq, int& idx) {
   seq = (int)((k >> 20) & 0xFFFFFull);
-  if (mode == 2) idx = (int)(0xFFFFFull - (k & 0xFFFFFull));
-  else idx = unkey_idx((int)(k & 0xFFFFFull));
+  if (mode == 1) idx = (int)(k & 0xFFFFFull);
+  else idx = unkey_idx((int)(0xFFFFFull - (k & 0xFFFFFull)));
 }
 
 }  // namespace sched

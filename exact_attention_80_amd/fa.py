@@ -229,9 +229,10 @@ def varlen_bwd_workspace(nseq: int, T: int, Hq: int, Hkv: int, d: int, causal: b
 
 
 def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, softmax_scale: float | None = None,
-               max_seqlen: int = 0, workspace: torch.Tensor | None = None):
+               max_seqlen: int = 0, workspace: torch.Tensor | None = None, lib=None):
     """Packed forward: q [T,Hq,d], k/v [T,Hkv,d], cu_seqlens int32 [nseq+1] on the device
-    -> (o [T,Hq,d], lse [Hq,T])."""
+    -> (o [T,Hq,d], lse [Hq,T]).  lib: another build of the library (load_variant)."""
+    L = _lib if lib is None else lib
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     _need(q, "q", (T, Hq, d))
@@ -242,19 +243,21 @@ def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, softmax_scale: float |
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
     ws = workspace
     if ws is None:
-        ws = varlen_fwd_workspace(nseq, T, Hq, Hkv, d, causal, q.device)
-    _check(_lib.fa_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              lse.data_ptr(), cu_seqlens.data_ptr(), nseq, T, int(max_seqlen),
-                              Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
-                              _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
-           "fa_varlen_fwd")
+        ws = _workspace(L.fa_varlen_fwd_workspace_size(nseq, T, Hq, Hkv, d, int(causal)), q.device)
+    _check(L.fa_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), cu_seqlens.data_ptr(), nseq, T, int(max_seqlen),
+                           Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
+                           _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+           "fa_varlen_fwd", L)
     return o, lse
 
 
 def varlen_bwd(q, k, v, o, lse, do, cu_seqlens, causal: bool = False,
                softmax_scale: float | None = None, deterministic: bool = False,
-               max_seqlen: int = 0, workspace: torch.Tensor | None = None):
-    """Packed backward -> (dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d])."""
+               max_seqlen: int = 0, workspace: torch.Tensor | None = None, lib=None):
+    """Packed backward -> (dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d]).  lib: another
+    build of the library (load_variant)."""
+    L = _lib if lib is None else lib
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     _need(q, "q", (T, Hq, d))
@@ -269,13 +272,14 @@ def varlen_bwd(q, k, v, o, lse, do, cu_seqlens, causal: bool = False,
     dv = torch.empty_like(v)
     ws = workspace
     if ws is None:
-        ws = varlen_bwd_workspace(nseq, T, Hq, Hkv, d, causal, deterministic, q.device)
-    _check(_lib.fa_varlen_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                              dv.data_ptr(), cu_seqlens.data_ptr(), nseq, T, int(max_seqlen),
-                              Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
-                              int(deterministic), ws.data_ptr(), ws.numel(), _stream()),
-           "fa_varlen_bwd")
+        n = L.fa_varlen_bwd_workspace_size(nseq, T, Hq, Hkv, d, int(causal), int(deterministic))
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(L.fa_varlen_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), cu_seqlens.data_ptr(), nseq, T, int(max_seqlen),
+                           Hq, Hkv, d, _scale(d, softmax_scale), int(causal),
+                           int(deterministic), ws.data_ptr(), ws.numel(), _stream()),
+           "fa_varlen_bwd", L)
     return dq, dk, dv
 
 
@@ -394,9 +398,11 @@ def varlen_qk_fwd_fp8(q8, k8, v, cu_seqlens_q, cu_seqlens_k, q_descale: float, k
 def varlen_qk_bwd(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
                   softmax_scale: float | None = None, deterministic: int | bool = False,
                   max_seqlen_q: int = 0, max_seqlen_k: int = 0,
-                  workspace: torch.Tensor | None = None):
+                  workspace: torch.Tensor | None = None, lib=None):
     """Packed backward with separate query and key lengths
-    -> (dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]); deterministic 0 or 1."""
+    -> (dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]); deterministic 0 or 1.
+    lib: another build of the library (load_variant)."""
+    L = _lib if lib is None else lib
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
     _need(q, "q", (Tq, Hq, d))
@@ -411,14 +417,16 @@ def varlen_qk_bwd(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, causal: bool 
     dv = torch.empty_like(v)
     ws = workspace
     if ws is None:
-        ws = varlen_qk_bwd_workspace(nseq, Tq, Tk, Hq, Hkv, d, causal, deterministic, q.device)
-    _check(_lib.fa_varlen_qk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                 do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                 dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
-                                 nseq, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
-                                 _scale(d, softmax_scale), int(causal), int(deterministic),
-                                 ws.data_ptr(), ws.numel(), _stream()),
-           "fa_varlen_qk_bwd")
+        n = L.fa_varlen_qk_bwd_workspace_size(nseq, Tq, Tk, Hq, Hkv, d, int(causal),
+                                              int(deterministic))
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(L.fa_varlen_qk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                              nseq, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
+                              _scale(d, softmax_scale), int(causal), int(deterministic),
+                              ws.data_ptr(), ws.numel(), _stream()),
+           "fa_varlen_qk_bwd", L)
     return dq, dk, dv
 
 

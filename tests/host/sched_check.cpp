@@ -25,13 +25,16 @@ int main() {
   for (int s = 0; s < nseq; ++s) {
     const int lq = cu_q[s + 1] - cu_q[s], lk = cu_k[s + 1] - cu_k[s];
     const int nt = seq_items(mode, causal != 0, cu_q.data(), cu_k.data(), s, tile, fkv);
+    // the cost the scheduler kernel passes: modes 0, 2 the sequence's largest
+    // tile cost, mode 1 the tile's own
     int seq_cost = 0;
-    if (mode == 2)
-      for (int k = 0; k < nt; ++k)
-        seq_cost = imax(seq_cost, item_cost(mode, causal != 0, lq, lk, tile, k, fkv, bq));
+    for (int k = 0; k < nt; ++k)
+      seq_cost = imax(seq_cost, item_cost(mode, causal != 0, lq, lk, tile,
+                                          seq_item_index(mode, causal != 0, lq, lk, tile, fkv, k),
+                                          fkv, bq));
     for (int k = 0; k < nt; ++k) {
       const int idx = seq_item_index(mode, causal != 0, lq, lk, tile, fkv, k);
-      const int cost = mode == 2 ? seq_cost : item_cost(mode, causal != 0, lq, lk, tile, idx, fkv, bq);
+      const int cost = mode == 1 ? item_cost(mode, causal != 0, lq, lk, tile, idx, fkv, bq) : seq_cost;
       keys.push_back(sort_key(mode, cost, s, idx));
     }
   }

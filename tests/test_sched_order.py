@@ -12,11 +12,13 @@ out here:
   * a forward tile costs its visible key tiles, a chunk its own key tiles, a
     backward key tile its visible query tiles of 32 rows, with the causal
     diagonal aligned bottom-right (query i sees key j iff j <= i + Lk - Lq);
-  * forward and fast backward: most expensive first, ties by sequence and
-    tile; deterministic backward: whole sequences, most expensive largest tile
-    first (ties by sequence), each sequence's key tiles together and last
-    first, so every key tile comes after all key tiles of its sequence that
-    its ordered dQ writes wait for.
+  * forward and deterministic backward: whole sequences in descending order
+    of their largest tile cost (ties by sequence), each sequence's items
+    together, the forward from the last query tile (split chunks first, last
+    chunk first), the deterministic backward from the last key tile, so every
+    key tile comes after all key tiles of its sequence that its ordered dQ
+    writes wait for; fast backward: every key tile most expensive first, ties
+    by sequence and tile.
 The order never changes results (tested on the GPU); these pins guard the
 progress argument of the ordered reduction and the load-balancing rule."""
 
@@ -85,12 +87,11 @@ def check(exe, mode, causal, lengths):
                for s, (lq, lk) in enumerate(lengths)}
     want = sorted((s, i, c) for s, items in per_seq.items() for i, c in items)
     assert sorted(got) == want, "items or costs differ from their definition"
-    if mode in (0, 1):
-        keys = [(-c, s, (i if i >= 0 else (1 << 19) - i - 1)) for s, i, c in got]
+    if mode == 1:
+        keys = [(-c, s, i) for s, i, c in got]
         assert keys == sorted(keys), "not most expensive first"
         return
-    # deterministic backward: sequences contiguous, longest largest tile first,
-    # key tiles last first
+    # sequences contiguous, in descending order of their largest tile cost
     seqs = []
     for s, i, c in got:
         if not seqs or seqs[-1] != s:
@@ -98,7 +99,10 @@ def check(exe, mode, causal, lengths):
             seqs.append(s)
     tiles = {s: [i for t, i, c in got if t == s] for s in seqs}
     for s in seqs:
-        assert tiles[s] == sorted(tiles[s], reverse=True), f"sequence {s} not last tile first"
+        # last tile first; forward split chunks (-(c + 1)) before the tiles, last chunk first
+        want_order = sorted(tiles[s], key=lambda i: (1 << 19) - i - 1 if i < 0 else i,
+                            reverse=True)
+        assert tiles[s] == want_order, f"sequence {s}: items out of order {tiles[s]}"
     big = [(-max(c for _, c in per_seq[s]), s) for s in seqs]
     assert big == sorted(big), "sequences not in descending order of their largest tile cost"
 
