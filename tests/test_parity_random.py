@@ -1,5 +1,6 @@
 """GPU parity on seeded random configurations: dense batches in every dQ
-mode, packed batches, and packed batches with separate query and key lengths,
+mode, packed batches, packed batches with separate query and key lengths, and
+the fp8-score forwards (dense and packed),
 with random head dimensions (64, 128, 256), GQA/MQA groupings, causal or not,
 and random lengths that include empty sequences, single tokens and ragged
 tails.  Each case is compared with the fp64 oracle at the same bars as the
@@ -125,3 +126,74 @@ def test_random_configuration(fa, case):
     if kind != "dense":
         empty = np.isneginf(rlse).T
         assert np.all(o[empty] == 0.0) and np.all(dq[empty] == 0.0)
+
+
+def _draw_fp8_cases(count=32, seed=2025):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2, 4]))
+        hq = hkv * int(rng.choice([1, 2, 4]))
+        causal = bool(rng.integers(2))
+        if i % 2 == 0:
+            cases.append((i, "dense", (int(rng.integers(1, 3)), int(rng.integers(1, 400))), hq, hkv,
+                          d, causal))
+        else:
+            n = int(rng.integers(1, 7))
+            lk = _lengths(rng, n, 2500)
+            lq = _lengths(rng, n, 200)
+            if sum(lq) == 0:
+                lq[0] = 1
+            if sum(lk) == 0:
+                lk[0] = 1
+            cases.append((i, "qk", (lq, lk), hq, hkv, d, causal))
+    return cases
+
+
+FP8_CASES = _draw_fp8_cases()
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"fp8-{c[0]}-{c[1]}")
+def test_random_fp8_forward(fa, case):
+    """The fp8-score forwards on random configurations (key lengths up to
+    2500, so split one-query tiles occur) against the oracle on the values
+    the e4m3 bytes stand for, at the bf16 forward's bars; the N(0, 1) draws
+    keep the score range far inside the one the LSE bar is claimed for."""
+    import torch
+    i, kind, shape, hq, hkv, d, causal = case
+    say(f"random fp8 case {i}: {kind} {shape} Hq={hq} Hkv={hkv} d={d} causal={causal}")
+    sc = scale_for(d)
+
+    def dev_bytes(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    if kind == "dense":
+        B, N = shape
+        x = inputs.fp8_dense_inputs(B, N, hq, hkv, d, seed=200 + i)
+        o, lse = fa.fwd_fp8(dev_bytes(x["q8"]), dev_bytes(x["k8"]), to_dev(x["v"]), x["q_descale"],
+                            x["k_descale"], causal=causal, softmax_scale=sc)
+        ro, rlse = ora.attention_forward(x["q"], x["k"], x["v"], sc, causal)
+        pv, _ = ora.attention_forward(x["q"], x["k"], np.abs(x["v"]), sc, causal)
+        n_keys = N
+    else:
+        lq, lk = shape
+        x = inputs.fp8_varlen_qk_inputs(lq, lk, hq, hkv, d, seed=200 + i)
+        cq = torch.from_numpy(x["cu_seqlens_q"]).to("cuda")
+        ck = torch.from_numpy(x["cu_seqlens_k"]).to("cuda")
+        o, lse = fa.varlen_qk_fwd_fp8(dev_bytes(x["q8"]), dev_bytes(x["k8"]), to_dev(x["v"]), cq, ck,
+                                      x["q_descale"], x["k_descale"], causal=causal,
+                                      softmax_scale=sc)
+        ro, rlse = ora.varlen_qk_forward(x["q"], x["k"], x["v"], x["cu_seqlens_q"],
+                                         x["cu_seqlens_k"], sc, causal)
+        pv, _ = ora.varlen_qk_forward(x["q"], x["k"], np.abs(x["v"]), x["cu_seqlens_q"],
+                                      x["cu_seqlens_k"], sc, causal)
+        n_keys = max(lk)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), to_host(lse)
+    errs = dict(o_excess=o_excess(o, ro, pv, n_keys), lse=_lse_error(lse, rlse))
+    say(f"errors {errs}")
+    assert np.all(np.isfinite(o))
+    assert errs["o_excess"] <= 1.0 and errs["lse"] <= TOL_LSE
+    if kind != "dense":
+        assert np.all(o[np.isneginf(rlse).T] == 0.0)
