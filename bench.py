@@ -807,6 +807,19 @@ def main():
                 fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale, lib=lib)
             kv = fa.timing_end(lib)["fwd"]
             extras[f"fwd_{name}_kernel_ms"] = kv[1] / max(1, kv[0])
+            if "fa_bwd.hip" in VARIANTS[name][0]:
+                o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
+                for tag, lb in (("", None), (f"{name}_", lib)):
+                    for _ in range(3):
+                        fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal,
+                               softmax_scale=scale, deterministic=det, lib=lb)
+                    torch.cuda.synchronize()
+                    fa.timing_begin(lb)
+                    for _ in range(args.steps):
+                        fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal,
+                               softmax_scale=scale, deterministic=det, lib=lb)
+                    kb = fa.timing_end(lb)["bwd_main"]
+                    extras[f"bwd_main_{tag or 'default_'}kernel_ms"] = kb[1] / max(1, kb[0])
 
     metric = METRIC
     if (B, N, Hq, Hkv, d, causal) != (2, 8192, 16, 16, 128, True):

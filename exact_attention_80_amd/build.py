@@ -30,6 +30,8 @@ VARIANTS = {
     # one exponential in four (or two) from the FMA-unit polynomial
     "exppoly4": (["fa_fwd.hip"], ["-DFA_EXP_POLY_EVERY=4"]),
     "exppoly2": (["fa_fwd.hip"], ["-DFA_EXP_POLY_EVERY=2"]),
+    # the d = 64 backward with 64 keys per wave (4 waves, one per SIMD)
+    "bwd64keys": (["fa_bwd.hip"], ["-DFA_BWD_KEY_BLOCKS=2"]),
 }
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.

@@ -421,8 +421,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1, 2 or 3");
   if (varlen && deterministic >= 2)
     return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 or 3 (partial-tile dQ) is dense-only");
-  if (d == 256 && deterministic >= 2)
-    return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 or 3 (partial-tile dQ) needs d <= 128");
+  if (deterministic >= 2 && !fa::bwd_partial_modes(d))
+    return fail(FA_ERR_UNSUPPORTED,
+                "deterministic == 2 or 3 (partial-tile dQ) needs d <= 128 and 32 keys per wave");
   const BwdLayout lay =
       bwd_layout(varlen, B, N, nseq, T, Tk, Hq, Hkv, d, deterministic, causal != 0);
   if (!ws || ws_bytes < lay.total)
@@ -575,7 +576,7 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
   if (deterministic < 0 || deterministic > 3) return 0;
-  if (d == 256 && deterministic >= 2) return 0;
+  if (deterministic >= 2 && !fa::bwd_partial_modes(d)) return 0;
   return bwd_layout(false, B, N, 0, (long)B * N, (long)B * N, Hq, Hkv, d, deterministic,
                     causal != 0).total;
 }

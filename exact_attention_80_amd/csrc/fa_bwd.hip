@@ -84,11 +84,24 @@ __device__ __forceinline__ int ds_off(int key, int s) {
   return key * (BQ * 2) + ((s ^ k ^ ((k & 2) << 1)) << 3);
 }
 
+// Key blocks of 32 per wave in the backward: 1 by default (8 waves, two per
+// SIMD).  A build with FA_BWD_KEY_BLOCKS=2 runs d = 64 with 4 waves of 64
+// keys (one wave per SIMD with its 512 registers), so that every Q and dO
+// operand read from LDS feeds the products of both key blocks; at d = 128
+// the two blocks' accumulators and operands do not fit 512 registers (about
+// 250 values spill), so d = 128 keeps one block.
+#ifndef FA_BWD_KEY_BLOCKS
+#define FA_BWD_KEY_BLOCKS 1
+#endif
+__host__ __device__ constexpr int bwd_key_blocks(int d) { return d == 64 ? FA_BWD_KEY_BLOCKS : 1; }
+__host__ __device__ constexpr int bwd_threads(int d) { return bwd_waves(d) / bwd_key_blocks(d) * 64; }
+
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
-__global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
-  constexpr int NW = bwd_waves(D);  // waves of 32 keys (shadows the d <= 128 defaults)
+__global__ __launch_bounds__(bwd_threads(D)) void bwd_kernel(BwdParams p) {
+  constexpr int KB = bwd_key_blocks(D);   // 32-key blocks per wave
+  constexpr int NW = bwd_waves(D) / KB;   // waves (shadows the d <= 128 defaults)
   constexpr int NT = NW * 64;
-  constexpr int BC = NW * 32;
+  constexpr int BC = NW * 32 * KB;
   // d = 256: each workgroup owns one half of the head dimension for dK, dV
   // and dQ (S and dP still use all of it), so its accumulators fit the
   // register file; two workgroups share a key tile
@@ -189,9 +202,17 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   const long q_row = (long)p.Hq * D;
   const long kv_row = (long)p.Hkv * D;
   const int key0 = it.jt * BC;
-  const int wk0 = key0 + wave * 32;  // this wave's first key
-  const int mykey = wk0 + l32;
-  const bool key_ok = mykey < it.k_len;
+  // block kb of this wave: keys wk0[kb] .. wk0[kb] + 31 (key rows of the
+  // workgroup's tile from krow0[kb])
+  int krow0[KB], wk0[KB], mykey[KB];
+  bool key_ok[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    krow0[kb] = (wave * KB + kb) * 32;
+    wk0[kb] = key0 + krow0[kb];
+    mykey[kb] = wk0[kb] + l32;
+    key_ok[kb] = mykey[kb] < it.k_len;
+  }
   const int klast = it.k_len - 1;  // last key row (row clamp of the K copy)
   const int qlast = it.q_len - 1;  // last query row
 
@@ -199,20 +220,24 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   const bf16* kseq = p.k + (long)it.k_start * kv_row + (long)it.hkv * D;
   const bf16* vseq = p.v + (long)it.k_start * kv_row + (long)it.hkv * D;
   dma_swz_tile<KT, KST, NW>(k_s, kseq, kv_row, key0, klast, wave, lane);
-  bf16x8 vf[D / 16];
+  bf16x8 vf[KB][D / 16];
 #pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc) {
-    u32x4 b = {0u, 0u, 0u, 0u};
-    if (key_ok) b = ld_global16(vseq + (long)mykey * kv_row + dc * 16 + half * 8);
-    vf[dc] = as_bf16x8(b);
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      u32x4 b = {0u, 0u, 0u, 0u};
+      if (key_ok[kb]) b = ld_global16(vseq + (long)mykey[kb] * kv_row + dc * 16 + half * 8);
+      vf[kb][dc] = as_bf16x8(b);
+    }
   wait_vmem();  // V rows and the K tile are in before the loop starts
 
-  f32x16 dk_acc[DH / 32], dv_acc[DH / 32];
+  f32x16 dk_acc[KB][DH / 32], dv_acc[KB][DH / 32];
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) { dk_acc[db][x] = 0.f; dv_acc[db][x] = 0.f; }
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) { dk_acc[kb][db][x] = 0.f; dv_acc[kb][db][x] = 0.f; }
 
   // ---------------- walk over (head, query tile); causal: from the first
   // query tile holding a query that sees key0 (query >= key0 - off)
@@ -276,7 +301,12 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   // indices).
   //   16-byte reads of chunk 2dc + half of row r:  base[dc & 1] + 64 (dc >> 1)
   const int q_rd[2] = {QT::off(l32, 8 * half), QT::off(l32, 16 + 8 * half)};
-  const int k_rd[2] = {KT::off(wave * 32 + l32, 8 * half), KT::off(wave * 32 + l32, 16 + 8 * half)};
+  int k_rd[KB][2];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    k_rd[kb][0] = KT::off(krow0[kb] + l32, 8 * half);
+    k_rd[kb][1] = KT::off(krow0[kb] + l32, 16 + 8 * half);
+  }
   //   transposed reads of Q/dO rows 16qc + 8ld + 4(g16/2) + L16/4, columns
   //   32db + 16(g16%2) + 4(L16%4):  base[ld] + 16 qc pitch + 64 db
   const int rq = 4 * (g16 >> 1) + (L16 >> 2);
@@ -455,85 +485,196 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
     const int h = h0 + hh;
     const int q0 = i * BQ;
 
-    const int koff = VARLEN ? it.off : 0;  // causal diagonal offset Lk - Lq
-    const bool active = wk0 < it.k_len && (!CAUSAL || q0 + BQ - 1 + koff >= wk0);
-    if (active) {
-      f32x16 s, dp;
+    if constexpr (KB == 1) {
+      const int koff = VARLEN ? it.off : 0;  // causal diagonal offset Lk - Lq
+      const bool active = wk0[0] < it.k_len && (!CAUSAL || q0 + BQ - 1 + koff >= wk0[0]);
+      if (active) {
+        f32x16 s, dp;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) { s[x] = 0.f; dp[x] = 0.f; }
+        for (int x = 0; x < 16; ++x) { s[x] = 0.f; dp[x] = 0.f; }
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        const int qo = q_rd[dc & 1] + 64 * (dc >> 1);
-        const bf16x8 aq = as_bf16x8(ld_lds16(qs + qo));
-        const bf16x8 bk = as_bf16x8(ld_lds16(k_s + k_rd[dc & 1] + 64 * (dc >> 1)));
-        const bf16x8 ado = as_bf16x8(ld_lds16(dos + qo));
-        s = mfma32x32x16(aq, bk, s);
-        dp = mfma32x32x16(ado, vf[dc], dp);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounds register pressure
-      // s[x] = S[q = q0 + 8(x/4) + 4 half + x%4][key = mykey]
-      const float* lse_s = reinterpret_cast<const float*>(sts);
-      const float* dv_s = lse_s + BQ;
-      const bool need_mask = (CAUSAL && q0 + koff < wk0 + 31) || (wk0 + 32 > it.k_len) ||
-                             (q0 + BQ > it.q_len);
-      // P = exp2(S c - LSE log2 e), dS = P o (dP - D); with a causal mask the
-      // masked copy runs on diagonal and ragged tiles only (a uniform branch)
-      auto softmax_grad = [&](auto masked) {
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const int qo = q_rd[dc & 1] + 64 * (dc >> 1);
+          const bf16x8 aq = as_bf16x8(ld_lds16(qs + qo));
+          const bf16x8 bk = as_bf16x8(ld_lds16(k_s + k_rd[0][dc & 1] + 64 * (dc >> 1)));
+          const bf16x8 ado = as_bf16x8(ld_lds16(dos + qo));
+          s = mfma32x32x16(aq, bk, s);
+          dp = mfma32x32x16(ado, vf[0][dc], dp);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounds register pressure
+        // s[x] = S[q = q0 + 8(x/4) + 4 half + x%4][key = mykey]
+        const float* lse_s = reinterpret_cast<const float*>(sts);
+        const float* dv_s = lse_s + BQ;
+        const bool need_mask = (CAUSAL && q0 + koff < wk0[0] + 31) || (wk0[0] + 32 > it.k_len) ||
+                               (q0 + BQ > it.q_len);
+        // P = exp2(S c - LSE log2 e), dS = P o (dP - D); with a causal mask the
+        // masked copy runs on diagonal and ragged tiles only (a uniform branch)
+        auto softmax_grad = [&](auto masked) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * g + 4 * half);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_s + 8 * g + 4 * half);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * g + 4 * half);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_s + 8 * g + 4 * half);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int x = 4 * g + e;
-            float pr = fast_exp2(fmaf(s[x], p.c, -l4[e]));
-            if (decltype(masked)::value) {
-              const int q = q0 + 8 * g + 4 * half + e;
-              if (!key_ok || q >= it.q_len || (CAUSAL && mykey > q + koff)) pr = 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int x = 4 * g + e;
+              float pr = fast_exp2(fmaf(s[x], p.c, -l4[e]));
+              if (decltype(masked)::value) {
+                const int q = q0 + 8 * g + 4 * half + e;
+                if (!key_ok[0] || q >= it.q_len || (CAUSAL && mykey[0] > q + koff)) pr = 0.f;
+              }
+              s[x] = pr;
+              dp[x] = pr * (dp[x] - d4[e]);
             }
-            s[x] = pr;
-            dp[x] = pr * (dp[x] - d4[e]);
+          }
+        };
+        if (CAUSAL && !need_mask) softmax_grad(std::false_type{});
+        else softmax_grad(std::true_type{});
+        bf16x8 pa[2], dsa[2];
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+          pa[qc] = frag_rows(s, qc);
+          dsa[qc] = frag_rows(dp, qc);
+        }
+        // dV += P^T dO and dK += dS^T Q over two 16-query chunks; the B operands
+        // are transposed reads of the row-major dO / Q tiles, rows
+        // 16qc + 8ld + 4half + 0..3 matching the registers of P and dS
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db) {
+            const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
+            const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
+            const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
+            const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
+            dv_acc[0][db] = mfma32x32x16(pa[qc], bdo, dv_acc[0][db]);
+            dk_acc[0][db] = mfma32x32x16(dsa[qc], bq, dk_acc[0][db]);
           }
         }
-      };
-      if (CAUSAL && !need_mask) softmax_grad(std::false_type{});
-      else softmax_grad(std::true_type{});
-      bf16x8 pa[2], dsa[2];
+        __builtin_amdgcn_sched_barrier(0);
+        // dS^T (bf16) rows of this wave's keys: the 4 consecutive queries of
+        // register group g are words 2(g%2), 2(g%2)+1 of dsa[g/2]
+        const int krow = wave * 32 + l32;
 #pragma unroll
-      for (int qc = 0; qc < 2; ++qc) {
-        pa[qc] = frag_rows(s, qc);
-        dsa[qc] = frag_rows(dp, qc);
-      }
-      // dV += P^T dO and dK += dS^T Q over two 16-query chunks; the B operands
-      // are transposed reads of the row-major dO / Q tiles, rows
-      // 16qc + 8ld + 4half + 0..3 matching the registers of P and dS
-#pragma unroll
-      for (int qc = 0; qc < 2; ++qc) {
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db) {
-          const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
-          const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
-          const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
-          const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
-          dv_acc[db] = mfma32x32x16(pa[qc], bdo, dv_acc[db]);
-          dk_acc[db] = mfma32x32x16(dsa[qc], bq, dk_acc[db]);
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 w4 = as_u32x4(dsa[g >> 1]);
+          const u32x2 w = (g & 1) ? u32x2{w4[2], w4[3]} : u32x2{w4[0], w4[1]};
+          st_lds8(dsd + ds_off(krow, 2 * g + half), w);
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // dS^T (bf16) rows of this wave's keys: the 4 consecutive queries of
-      // register group g are words 2(g%2), 2(g%2)+1 of dsa[g/2]
-      const int krow = wave * 32 + l32;
+      } else {
+        const int krow = wave * 32 + l32;
+        const u32x2 z = {0u, 0u};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x4 w4 = as_u32x4(dsa[g >> 1]);
-        const u32x2 w = (g & 1) ? u32x2{w4[2], w4[3]} : u32x2{w4[0], w4[1]};
-        st_lds8(dsd + ds_off(krow, 2 * g + half), w);
+        for (int g = 0; g < 4; ++g) st_lds8(dsd + ds_off(krow, 2 * g + half), z);
       }
     } else {
-      const int krow = wave * 32 + l32;
-      const u32x2 z = {0u, 0u};
+      const int koff = VARLEN ? it.off : 0;  // causal diagonal offset Lk - Lq
+      // a block whose keys all lie past the sequence end or (causal) after
+      // every query of the tile contributes nothing; with several blocks per
+      // wave the products still run for all of them when any is active (the
+      // mask then zeroes the inactive ones)
+      bool active = false;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) st_lds8(dsd + ds_off(krow, 2 * g + half), z);
+      for (int kb = 0; kb < KB; ++kb)
+        active |= wk0[kb] < it.k_len && (!CAUSAL || q0 + BQ - 1 + koff >= wk0[kb]);
+      if (active) {
+        f32x16 s[KB], dp[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) { s[kb][x] = 0.f; dp[kb][x] = 0.f; }
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const int qo = q_rd[dc & 1] + 64 * (dc >> 1);
+          const bf16x8 aq = as_bf16x8(ld_lds16(qs + qo));
+          const bf16x8 ado = as_bf16x8(ld_lds16(dos + qo));
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 bk = as_bf16x8(ld_lds16(k_s + k_rd[kb][dc & 1] + 64 * (dc >> 1)));
+            s[kb] = mfma32x32x16(aq, bk, s[kb]);
+            dp[kb] = mfma32x32x16(ado, vf[kb][dc], dp[kb]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounds register pressure
+        // s[kb][x] = S[q = q0 + 8(x/4) + 4 half + x%4][key = mykey[kb]]
+        const float* lse_s = reinterpret_cast<const float*>(sts);
+        const float* dv_s = lse_s + BQ;
+        // P = exp2(S c - LSE log2 e), dS = P o (dP - D); with a causal mask the
+        // masked copy runs on diagonal and ragged tiles only (a uniform branch)
+        auto softmax_grad = [&](auto masked, f32x16& sk, f32x16& dpk, int mk,
+                                bool kok) __attribute__((always_inline)) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * g + 4 * half);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv_s + 8 * g + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int x = 4 * g + e;
+              float pr = fast_exp2(fmaf(sk[x], p.c, -l4[e]));
+              if (decltype(masked)::value) {
+                const int q = q0 + 8 * g + 4 * half + e;
+                if (!kok || q >= it.q_len || (CAUSAL && mk > q + koff)) pr = 0.f;
+              }
+              sk[x] = pr;
+              dpk[x] = pr * (dpk[x] - d4[e]);
+            }
+          }
+        };
+        bf16x8 pa[KB][2], dsa[KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bool need_mask = (CAUSAL && q0 + koff < wk0[kb] + 31) || (wk0[kb] + 32 > it.k_len) ||
+                                 (q0 + BQ > it.q_len);
+          if (CAUSAL && !need_mask)
+            softmax_grad(std::false_type{}, s[kb], dp[kb], mykey[kb], key_ok[kb]);
+          else
+            softmax_grad(std::true_type{}, s[kb], dp[kb], mykey[kb], key_ok[kb]);
+#pragma unroll
+          for (int qc = 0; qc < 2; ++qc) {
+            pa[kb][qc] = frag_rows(s[kb], qc);
+            dsa[kb][qc] = frag_rows(dp[kb], qc);
+          }
+        }
+        // dV += P^T dO and dK += dS^T Q over two 16-query chunks; the B operands
+        // are transposed reads of the row-major dO / Q tiles, rows
+        // 16qc + 8ld + 4half + 0..3 matching the registers of P and dS, shared
+        // by the key blocks
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db) {
+            const int o0 = q_tr[0] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
+            const int o1 = q_tr[1] + 16 * qc * QT::kPitch + 2 * dh0 + 64 * db;
+            const bf16x8 bdo = cat8(ld_lds_tr8(dos + o0), ld_lds_tr8(dos + o1));
+            const bf16x8 bq = cat8(ld_lds_tr8(qs + o0), ld_lds_tr8(qs + o1));
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dv_acc[kb][db] = mfma32x32x16(pa[kb][qc], bdo, dv_acc[kb][db]);
+              dk_acc[kb][db] = mfma32x32x16(dsa[kb][qc], bq, dk_acc[kb][db]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dS^T (bf16) rows of this wave's keys: the 4 consecutive queries of
+        // register group g are words 2(g%2), 2(g%2)+1 of dsa[kb][g/2]
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int krow = krow0[kb] + l32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x4 w4 = as_u32x4(dsa[kb][g >> 1]);
+            const u32x2 w = (g & 1) ? u32x2{w4[2], w4[3]} : u32x2{w4[0], w4[1]};
+            st_lds8(dsd + ds_off(krow, 2 * g + half), w);
+          }
+        }
+      } else {
+        const u32x2 z = {0u, 0u};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int krow = krow0[kb] + l32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) st_lds8(dsd + ds_off(krow, 2 * g + half), z);
+        }
+      }
     }
   };
 
@@ -666,30 +807,32 @@ __global__ __launch_bounds__(bwd_waves(D) * 64) void bwd_kernel(BwdParams p) {
   }
 
   // ---------------- dK = scale * sum dS^T Q, dV = sum P^T dO for this wave's keys
-  // dk_acc[db][x] = dK[key = wk0 + 8(x/4) + 4 half + x%4][d = dh0 + 32 db + l32]
+  // dk_acc[kb][db][x] = dK[key = wk0[kb] + 8(x/4) + 4 half + x%4][d = dh0 + 32 db + l32]
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int key = wk0 + 8 * (x >> 2) + 4 * half + (x & 3);
-      if (key < it.k_len) {
-        const long off =
-            ((long)it.k_start + key) * kv_row + (long)it.hkv * D + dh0 + db * 32 + l32;
-        if (p.S == 1) {
-          p.dk[off] = (bf16)(dk_acc[db][x] * p.scale);
-          p.dv[off] = (bf16)(dv_acc[db][x]);
-        } else {
-          const long po = (long)it.split * p.Tk * kv_row + off;
-          p.dk_part[po] = dk_acc[db][x] * p.scale;
-          p.dv_part[po] = dv_acc[db][x];
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int key = wk0[kb] + 8 * (x >> 2) + 4 * half + (x & 3);
+        if (key < it.k_len) {
+          const long off =
+              ((long)it.k_start + key) * kv_row + (long)it.hkv * D + dh0 + db * 32 + l32;
+          if (p.S == 1) {
+            p.dk[off] = (bf16)(dk_acc[kb][db][x] * p.scale);
+            p.dv[off] = (bf16)(dv_acc[kb][db][x]);
+          } else {
+            const long po = (long)it.split * p.Tk * kv_row + off;
+            p.dk_part[po] = dk_acc[kb][db][x] * p.scale;
+            p.dv_part[po] = dv_acc[kb][db][x];
+          }
         }
       }
-    }
 }
 
 template <int D, bool CAUSAL, bool VARLEN, int DQM>
 hipError_t launch_bwd_t(const BwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, VARLEN, DQM>), dim3(grid), dim3(bwd_waves(D) * 64), 0,
+  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, VARLEN, DQM>), dim3(grid), dim3(bwd_threads(D)), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -697,7 +840,7 @@ hipError_t launch_bwd_t(const BwdParams& p, int grid, hipStream_t stream) {
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_mode(const BwdParams& p, int mode, int grid, hipStream_t stream) {
   if (mode == kDqOrdered) return launch_bwd_t<D, CAUSAL, VARLEN, kDqOrdered>(p, grid, stream);
-  if constexpr (D != 256) {  // the partial-tile modes take d <= 128
+  if constexpr (D != 256 && bwd_key_blocks(D) == 1) {  // partial tiles: 32 keys per wave
     if (mode == kDqPartial && !VARLEN)
       return launch_bwd_t<D, CAUSAL, false, kDqPartial>(p, grid, stream);
     if (mode == kDqFused && !VARLEN)
@@ -949,6 +1092,8 @@ hipError_t launch_bwd_dq_reduce(const float* part, bf16* dq, int B, int N, int H
   }
   return hipGetLastError();
 }
+
+bool bwd_partial_modes(int d) { return d != 256 && bwd_key_blocks(d) == 1; }
 
 long bwd_partial_pairs(int N, bool causal) {
   const int nq = (N + kBwdBQ - 1) / kBwdBQ, nkv = (N + kBwdBC - 1) / kBwdBC;

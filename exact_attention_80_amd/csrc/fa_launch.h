@@ -76,6 +76,9 @@ hipError_t launch_bwd_dq_reduce(const float* part, bf16* dq, int B, int N, int H
 // partial dQ tiles per (batch, query head) in mode 2
 long bwd_partial_pairs(int N, bool causal);
 
+// whether this build offers the partial-tile dQ modes (2, 3) for head dim d
+bool bwd_partial_modes(int d);
+
 // dQ = bf16(scale * dQ_acc); when S > 1 also dK/dV = bf16(sum of the S partials).
 // dq_elems counts query-side elements, kv_elems key-side ones.
 hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float scale,

@@ -39,7 +39,9 @@
  *    non-decreasing) and a violation is reported through the workspace error
  *    word (fa_workspace_error), not by the return value.
  *  - d (head dimension) is 64, 128 or 256 (256: the fa_bwd partial-tile modes
- *    deterministic == 2, 3 are not offered; the fp8 forwards take 64 or 128).
+ *    deterministic == 2, 3 are not offered, nor at d = 64 in a library built
+ *    with 64 keys per backward wave (FA_BWD_KEY_BLOCKS=2); the fp8 forwards
+ *    take 64 or 128).
  *    Hq must be a positive multiple of Hkv, and Hq * d below 2^24 (per-tile
  *    buffer ranges are 32-bit; larger shapes return FA_ERR_UNSUPPORTED);
  *    query head h uses key/value head h / (Hq/Hkv) ([FA2] "Core method" 4).
