@@ -9,8 +9,9 @@
 //    32 keys and keeps its
 //    K and V rows and its dK, dV accumulators in registers for the whole
 //    kernel.  The workgroup walks every query head of its key/value head
-//    (subgroup) and, per head, the 32-row query tiles from the diagonal
-//    upwards (causal) or all of them; per query tile:
+//    (subgroup) and, per head, the 32-row query tiles that see its keys
+//    (causal: from the last one down to the diagonal, or from the diagonal
+//    up in the ordered mode below) or all of them; per query tile:
 //        S  = Q K^T,  P = exp2(S c - LSE log2 e)        (recomputed, masked)
 //        dP = dO V^T, dS = P o (dP - D)
 //        dV += P^T dO,  dK += dS^T Q                    (register accumulators)
@@ -23,11 +24,12 @@
 //    Workgroups take their work items from an atomic ticket in that same
 //    descending order, so every workgroup a writer waits for already runs and
 //    the causal walk (diagonal first) never stalls on its first write.
-//    A third way (fused partial sums) needs neither atomics on dQ nor a
-//    second kernel: every workgroup stores its fp32 partial tile, counts
-//    itself in with one atomic per tile once its stores are complete, and the
-//    last contributor of a query tile sums all partial tiles in ascending
-//    key-tile order and writes bf16 dQ (deterministic by construction).
+//    Two more deterministic ways need no atomic adds on dQ: every workgroup
+//    stores its fp32 partial tile, and either a second kernel sums each
+//    query tile's partial tiles in ascending key-tile order, or (fused) each
+//    workgroup counts itself in with one atomic per tile once its stores are
+//    complete and the last contributor of a query tile does that sum and
+//    writes bf16 dQ itself.
 //  * post: dQ = bf16(scale * dQ_acc); split subgroups' dK/dV partials are
 //    summed in a fixed order.
 // A packed sequence may have Lq queries and Lk keys (the decode-shaped
@@ -54,10 +56,9 @@ constexpr int BC = kBwdBC;
 // dwords) filled by direct global->LDS loads; Q/dO/LSE/D are double
 // buffered.  dS^T is written by the waves with 8-byte stores into 64-byte rows
 // whose 8-byte slots are permuted by the row's quad index (conflict-free for
-// both the stores and the transposed reads).  The waves that own the second
-// key half of a dQ column block leave their partial sums in `part` for the
-// first half's wave to add before its atomics.  d = 128: 81920 + 4 x 10240 +
-// 512 + 16384 + 16384 bytes.
+// both the stores and the transposed reads); it is double buffered too, so
+// that an item's dQ products can read it while the next item writes its own.
+// d = 128: 81920 + 4 x 10240 + 512 + 16384 + 16384 bytes.
 template <int D>
 struct BwdLds {
   static constexpr int BCD = bwd_tile_keys(D);       // keys per workgroup
