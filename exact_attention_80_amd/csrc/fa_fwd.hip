@@ -10,8 +10,9 @@
 //    register staging) into padded tiles, through a ring of fwd_stages(D)
 //    buffers (4; 2 for d = 256, whose tiles are twice as large): the next
 //    tiles are in flight while tile j is computed; with 8 waves the first
-//    four issue all copies, after their own products of a tile (they run
-//    ahead of their SIMD partners, which are the critical path);
+//    four issue all copies: with the 4-deep ring after their own products
+//    of a tile (they run ahead of their SIMD partners, which are the
+//    critical path), with the 2-deep ring right after the barrier;
 //  * a tile's K operands (and the first V^T operands) are read into
 //    registers in one batch before its products;
 //  * the score tile is computed transposed, S^T = K Q^T, so each lane holds one
