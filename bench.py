@@ -20,8 +20,8 @@ Prints one JSON line.  Besides the headline it carries:
   extras        per-kernel times; in the atomic mode also the bytes of fp32 dQ
                 atomic adds per backward launch and the rate they imply, to
                 set beside what the atomics alone sustain (--atomic-probe):
-                that kernel has two co-bounds, its dQ atomic traffic and its
-                own compute path, both close to its measured time;
+                that kernel is bound by its dQ atomic traffic (its other
+                work takes well under its measured time);
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample (whole query
                 heads of the same workload) on this host's cores, scaled to the
                 metric's unit.
@@ -743,7 +743,7 @@ def main():
     if det == 0:
         # the fast mode's dQ reduction: device-scope fp32 atomic adds; the
         # rate they imply over the kernel's time, against what they sustain
-        # alone (--atomic-probe), is one of the kernel's two co-bounds
+        # alone (--atomic-probe), shows how close the kernel is to that bound
         dq_bytes = dq_reduction_bytes(B, N, Hq, d, causal)
         extras["bwd_dq_atomic_bytes"] = dq_bytes
         extras["bwd_dq_atomic_tbps"] = dq_bytes / (avg_bwd_ms * 1e-3) / 1e12
