@@ -869,12 +869,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
                                                       uint32_t* hdr, int rows, int Hq, bool varlen,
                                                       int N, int T) {
   constexpr int EPT = D / 16;  // elements per thread (16 threads per row)
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  // a block takes 16 consecutive tokens of one query head, so that its D
+  // and LSE values are 16 consecutive floats of their [b, h, n] arrays
+  const int h = blockIdx.x % Hq;
+  const int tok = (blockIdx.x / Hq) * 16 + (threadIdx.x >> 4);
+  const int row = tok * Hq + h;
   const int sub = threadIdx.x & 15;
   if (blockIdx.x == 0 && threadIdx.x < kHdrWords) hdr[threadIdx.x] = 0u;
   for (long s = (long)blockIdx.x * 256 + threadIdx.x; s < sem_count; s += (long)gridDim.x * 256)
     sem[s] = 0;
-  if (row >= rows) return;
+  if (tok >= rows / Hq) return;
   const long base = (long)row * D + sub * EPT;
   float acc = 0.f;
   if (EPT == 8) {
@@ -896,7 +900,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
     for (int e = 0; e < EPT; e += 4) *reinterpret_cast<f32x4*>(dq_acc + base + e) = z;
   }
   if (sub == 0) {
-    const int tok = row / Hq, h = row - tok * Hq;
     long idx;
     if (varlen) idx = (long)h * T + tok;
     else {
@@ -1106,7 +1109,7 @@ long bwd_partial_pairs(int N, bool causal) {
 hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, float* dvec,
                           float* lse2, float* dq_acc, int* sem, long sem_count, uint32_t* hdr,
                           int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream) {
-  const int grid = max(1, (rows + 15) / 16);
+  const int grid = max(1, Hq * ((rows / Hq + 15) / 16));
   if (d == 256)
     hipLaunchKernelGGL(bwd_pre_kernel<256>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
                        lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
