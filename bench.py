@@ -500,6 +500,9 @@ def run_sweep(args):
             cpu_cache[key] = (cpu_baseline(B, N, Hq, Hkv, d, causal, args.cpu_budget)
                               if args.cpu_budget > 0 else None)
         scheds = ("longest-first", "natural") if cid == "H" else ("longest-first",)
+        # one discarded run first, so that the first timed row is as warm as
+        # the others (clocks, first touch of the new buffers)
+        measure_dense(fa, x, B, N, Hq, Hkv, d, causal, 0, max(10, args.steps), args.warmup)
         for det in (0, 1):
             for sched in scheds:
                 if sched == "natural":
@@ -530,6 +533,8 @@ def run_sweep(args):
     f_fwd, f_bwd = varlen_flops(lengths, Hq, d, True)
     cpu = (varlen_cpu_baseline(xv, lengths, Hq, Hkv, d, True, args.cpu_budget)
            if args.cpu_budget > 0 else None)
+    measure_varlen(fa, t, cu, lengths, Hq, Hkv, d, True, 0, max(10, args.steps),
+                   args.warmup)  # discarded, as for the dense workloads
     for det in (0, 1):
         for sched in ("longest-first", "natural"):
             if sched == "natural":
