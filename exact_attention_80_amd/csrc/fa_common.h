@@ -269,32 +269,44 @@ __host__ __device__ __forceinline__ uint32_t tile_range(int row0, int len, long 
 }
 
 // Per-lane offsets of the uniform-count copy of one tile (see dma_count):
-// computed once, reused for every tile of the same geometry.
-template <class T, int NW>
+// computed once, reused for every tile of the same geometry.  They are held
+// in registers, or (IN_LDS, for kernels with no register to spare across the
+// tile loop) in an LDS array of kStash dwords per lane, read back before each
+// copy: the wave that writes a lane's offsets is the only one that reads them.
+template <class T, int NW, bool IN_LDS = false>
 struct TileCopy {
   static constexpr int kN = (T::kInstr + NW - 1) / NW;
   static constexpr int kLastLanes = T::kSlots - (T::kInstr - 1) * 64;  // lanes used by the last
-  uint32_t voff[kN];
+  static constexpr int kStash = kN * NW * 64;  // dwords of the LDS array (IN_LDS)
+  uint32_t voff[IN_LDS ? 1 : kN];
+  uint32_t* stash_;  // IN_LDS: this lane's k-th offset at stash_[k * NW * 64]
   int wave_, lane_;
+  // `stash` (IN_LDS): the kStash-dword LDS array; `writer`: this wave fills
+  // its part of it (waves that never copy leave it alone)
   template <class ChunkOf>
   __device__ __forceinline__ void init(long row_bytes, int stride, int wave, int lane,
-                                       ChunkOf chunk_of) {
+                                       ChunkOf chunk_of, uint32_t* stash = nullptr,
+                                       bool writer = true) {
     wave_ = wave;
     lane_ = lane;
+    stash_ = IN_LDS ? stash + wave * 64 + lane : nullptr;
 #pragma unroll
     for (int k = 0; k < kN; ++k) {
       const int s = min(k * NW + wave, T::kInstr - 1) * 64 + lane;
       const int row = s / stride;
       int c = chunk_of(row, s - row * stride);
       if (c < 0) c = 0;
-      voff[k] = (uint32_t)(row * row_bytes + c * 16);
+      const uint32_t o = (uint32_t)(row * row_bytes + c * 16);
+      if (!IN_LDS) voff[k] = o;
+      else if (writer) stash_[k * NW * 64] = o;
     }
   }
   __device__ __forceinline__ void issue(char* dst, i32x4 rsrc) const {
 #pragma unroll
     for (int k = 0; k < kN; ++k) {
       const int kk = min(k * NW + wave_, T::kInstr - 1);  // wave-uniform
-      if (kk < T::kInstr - 1 || lane_ < kLastLanes) dma16_buf(rsrc, voff[k], dst + kk * 1024);
+      const uint32_t o = IN_LDS ? stash_[k * NW * 64] : voff[k];
+      if (kk < T::kInstr - 1 || lane_ < kLastLanes) dma16_buf(rsrc, o, dst + kk * 1024);
     }
   }
 };

@@ -225,10 +225,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const bool copier = wave < CW;
   const long kv_bytes = kv_row * 2;     // V row pitch (bf16)
   const long k_bytes = kv_row * EB;     // K row pitch
-  TileCopy<KT, CW> kcopy;
-  TileCopy<VT, CW> vcopy;
-  kcopy.init(k_bytes, KCH + 1, wave % CW, lane, [](int, int pc) { return pc < KCH ? pc : -1; });
-  vcopy.init(kv_bytes, VST, wave % CW, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); });
+  // d = 256 holds the copy offsets in LDS: its products leave no register
+  // free across the tile loop, and offsets spilled to scratch would be
+  // reloaded with a wait that also drains the tile copies in flight
+  constexpr bool OFF_LDS = D == 256;
+  using KCopy = TileCopy<KT, CW, OFF_LDS>;
+  using VCopy = TileCopy<VT, CW, OFF_LDS>;
+  __shared__ uint32_t off_s[OFF_LDS ? KCopy::kStash + VCopy::kStash : 1];
+  KCopy kcopy;
+  VCopy vcopy;
+  kcopy.init(k_bytes, KCH + 1, wave % CW, lane, [](int, int pc) { return pc < KCH ? pc : -1; },
+             off_s, copier);
+  vcopy.init(kv_bytes, VST, wave % CW, lane, [](int row, int pc) { return VT::slot_chunk(row, pc); },
+             off_s + KCopy::kStash, copier);
   auto issue_tile = [&](int u) {  // the u-th tile of this item, key tile jb + u
     if (!copier) return;
     char* kt = kv_s[u % STAGES];

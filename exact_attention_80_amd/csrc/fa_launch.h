@@ -9,9 +9,10 @@ namespace fa {
 
 constexpr int kFwdWaves = 8;   // forward workgroup: 8 waves, 256 query rows
 constexpr int kFwdStages = 4;  // forward K/V copy ring depth (tiles)
-// d = 256 also runs 8 waves (two per SIMD; about 16 values spill, against the
-// one wave per SIMD that 512 registers would allow: 0.29 against 0.36 ms at
-// B = 2, H = 16, N = 4096 causal) and a 2-deep ring of 70 KB K/V tiles
+// d = 256 also runs 8 waves (two per SIMD, rather than the one wave per SIMD
+// that 512 registers would allow: 0.29 against 0.36 ms at B = 2, H = 16,
+// N = 4096 causal even before the copy offsets moved to LDS) and a 2-deep
+// ring of 70 KB K/V tiles
 __host__ __device__ constexpr int fwd_waves(int) { return kFwdWaves; }
 __host__ __device__ constexpr int fwd_stages(int d) { return d == 256 ? 2 : kFwdStages; }
 constexpr int kBwdWaves = 8;   // backward workgroup (d <= 128): 8 waves, 256 keys
