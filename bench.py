@@ -1,8 +1,10 @@
 """Benchmark: causal self-attention forward + backward on one MI355X.
 
 One step = one forward and one backward pass over one batch of the headline
-workload (B=2, H=16, N=8192, d=128, bf16, causal, fast-mode backward), with
-seeded synthetic inputs already resident in HBM.  Throughput counts the
+workload (B=2, H=16, N=8192, d=128, bf16, causal), with seeded synthetic
+inputs already resident in HBM.  The backward reduces dQ across key tiles with
+int32 fixed-point atomic adds by default (--dq-mode 4: the fastest of the
+modes here, and bit-reproducible); --dq-mode 0 selects fp32 atomics.  Throughput counts the
 algorithmic FLOPs 4*B*H*N^2*d/2 (forward) + 2.5x that (backward).
 
 With --workload decode the step is instead one forward and one backward over
@@ -17,20 +19,21 @@ Prints one JSON line.  Besides the headline it carries:
                 MFMA peak; `traffic` is the kernel's HBM bytes per launch from
                 the recorded rocprofv3 counter runs (profiles/), or null when
                 the kernel sources changed since they were taken;
-  extras        per-kernel times; in the atomic mode also the bytes of fp32 dQ
+  extras        per-kernel times; in the atomic modes also the bytes of dQ
                 atomic adds per backward launch and the rate they imply, to
                 set beside what the atomics alone sustain (--atomic-probe):
-                that kernel is bound by its dQ atomic traffic (its other
-                work takes well under its measured time);
+                the dQ adds alone take most of that kernel's time (fp32) or
+                well over half of it (int32), so they bound it together with
+                its products;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample (whole query
                 heads of the same workload) on this host's cores, scaled to the
                 metric's unit.
 
 Other modes: --sweep prints one line per measured workload (MHA 2K, the
 headline, long context 16K/32K, GQA/MQA, the 65536-token packed batch; fast and
-ordered dQ; with and without the longest-first tile order); --atomic-probe
-measures the backward's dQ atomic adds alone against plain stores of the same
-bytes; --device-info prints the CU count and clock; --workload decode times a
+ordered and fixed-point dQ; with and without the longest-first tile order);
+--atomic-probe measures the backward's fp32 and int32 dQ atomic adds alone
+against plain stores of the same bytes; --device-info prints the CU count and clock; --workload decode times a
 packed batch with separate query and key lengths.
 """
 
@@ -58,6 +61,9 @@ def flops(B, N, H, d, causal):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.txt")
+# the backward's dQ reductions (the `deterministic` argument)
+DQ_MODE_NAMES = ("atomic", "semaphore-ordered", "partial-tile", "fused partial-tile",
+                 "fixed-point atomic")
 KERNEL_SOURCES = ("fa_bwd.hip", "fa_common.h", "fa_launch.h")
 
 
@@ -241,7 +247,7 @@ def run_decode(args):
 
     Hq, Hkv, d = 32, 4, 128
     det = args.dq_mode
-    if det >= 2:
+    if det in (2, 3):
         print("bench.py: the partial-tile dQ reductions are dense-only", file=sys.stderr)
         sys.exit(2)
     lq, lk = inputs.qk_lengths()
@@ -330,7 +336,7 @@ def run_decode(args):
             "workload": f"causal packed batch with separate query and key lengths: {len(lq)} "
                         f"sequences, {Tq} queries against {Tk} keys (half one-query decode steps), "
                         f"Hq={Hq} Hkv={Hkv} d={d}, "
-                        f"{('atomic', 'semaphore-ordered')[det]} dQ reduction",
+                        f"{DQ_MODE_NAMES[det]} dQ reduction",
             "nseq": len(lq), "total_q": Tq, "total_k": Tk, "Hq": Hq, "Hkv": Hkv, "d": d,
             "causal": True, "deterministic": det,
         },
@@ -462,7 +468,7 @@ def sweep_line(cid, workload, value_flops, ms_step, avg, f_fwd, f_bwd, det, sche
     fwd_ms = avg.get("fwd_total", avg["fwd"])
     line = {
         "sweep": cid, "workload": workload,
-        "dq_reduction": ("atomic", "semaphore-ordered", "partial-tile", "fused partial-tile")[det],
+        "dq_reduction": DQ_MODE_NAMES[det],
         "tile_order": sched,
         "value": value_flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
         "pct_of_peak": 100.0 * value_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -481,8 +487,8 @@ def sweep_line(cid, workload, value_flops, ms_step, avg, f_fwd, f_bwd, det, sche
 def run_sweep(args):
     """One JSON line per workload of the scope table's measurement row: MHA 2K
     (d = 64, 128; causal and not), the headline, long context 16K / 32K, GQA
-    / MQA, and the 65536-token packed batch; each in the fast (atomic) and the
-    deterministic (semaphore-ordered) mode, plus the headline and the packed
+    / MQA, and the 65536-token packed batch; each with fp32 atomic,
+    semaphore-ordered and fixed-point dQ, plus the headline and the packed
     batch with the longest-first tile order switched off (FA_SCHED=natural)."""
     import torch
 
@@ -503,7 +509,7 @@ def run_sweep(args):
         # one discarded run first, so that the first timed row is as warm as
         # the others (clocks, first touch of the new buffers)
         measure_dense(fa, x, B, N, Hq, Hkv, d, causal, 0, max(10, args.steps), args.warmup)
-        for det in (0, 1):
+        for det in (0, 1, 4):
             for sched in scheds:
                 if sched == "natural":
                     os.environ["FA_SCHED"] = "natural"
@@ -535,7 +541,7 @@ def run_sweep(args):
            if args.cpu_budget > 0 else None)
     measure_varlen(fa, t, cu, lengths, Hq, Hkv, d, True, 0, max(10, args.steps),
                    args.warmup)  # discarded, as for the dense workloads
-    for det in (0, 1):
+    for det in (0, 1, 4):
         for sched in ("longest-first", "natural"):
             if sched == "natural":
                 os.environ["FA_SCHED"] = "natural"
@@ -551,23 +557,24 @@ def run_sweep(args):
 
 
 def run_atomic_probe(args):
-    """What the fast backward's dQ reduction can sustain: its fp32 atomic adds
+    """What the backward's dQ reductions can sustain: its fp32 atomic adds
     alone (same instructions, same 32 x 16 per-wave blocks of a [rows, Hq*d]
-    fp32 accumulator, 1024 workgroups), against plain stores of the same
-    bytes; the headline backward moves 2.21 GB this way per launch."""
+    fp32 accumulator, 1024 workgroups), the fixed-point mode's int32 atomic
+    adds in the same pattern, and plain stores of the same bytes; the
+    headline backward moves 2.21 GB this way per launch."""
     import torch
 
     from exact_attention_80_amd import fa
     torch.cuda.set_device(0)
     rows, row_floats = 2 * 8192, 16 * 128          # the headline's dQ accumulator
-    buf = torch.zeros((rows, row_floats), dtype=torch.float32, device="cuda")
     blocks, items = 1024, 132                     # 1024 x 132 x 16 KiB = 2.21 GB
     out = {"probe": "dq_reduction", "rows": rows, "row_floats": row_floats,
            "blocks": blocks, "items": items}
-    launches = 0
-    for store in (False, True):
+    for kind, key in ((0, "atomic"), (2, "int_atomic"), (1, "store")):
+        buf = torch.zeros((rows, row_floats), dtype=torch.float32, device="cuda")
+        launches = 0
         for _ in range(2):
-            fa.probe_dq_reduction(buf, blocks, items, store)
+            fa.probe_dq_reduction(buf, blocks, items, kind)
         launches += 2
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -575,23 +582,24 @@ def run_atomic_probe(args):
         reps = 10
         nbytes = 0
         for _ in range(reps):
-            nbytes += fa.probe_dq_reduction(buf, blocks, items, store)
+            nbytes += fa.probe_dq_reduction(buf, blocks, items, kind)
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
         launches += reps
-        key = "store" if store else "atomic"
         out[f"{key}_ms"] = ms
         out[f"{key}_tbps"] = nbytes / reps / (ms * 1e-3) / 1e12
         out["bytes_per_launch"] = nbytes // reps
-        if not store:
-            # every atomic launch added 1/1024 to each element of the 4096-element
-            # tiles it visited (sums exact in fp32): all adds landed
-            want = launches * blocks * items * 4096 / 1024
-            got = float(buf.double().sum())
-            out["atomic_sum_check"] = got == want
+        if kind != 1:
+            # every atomic launch added 1/1024 (fp32) or 1 (int32) to each
+            # element of the 4096-element tiles it visited, exactly: all adds landed
+            per = 1.0 / 1024 if kind == 0 else 1.0
+            want = launches * blocks * items * 4096 * per
+            got = float((buf if kind == 0 else buf.view(torch.int32)).double().sum())
+            out[f"{key}_sum_check"] = got == want
             if got != want:
-                raise RuntimeError(f"probe sum {got} != {want}")
+                raise RuntimeError(f"probe sum {got} != {want} ({key})")
+        del buf
     print(json.dumps(out), flush=True)
 
 
@@ -625,17 +633,18 @@ def main():
                     help="headline: causal B=2 H=16 N=8192 d=128; decode: packed batch with "
                          "separate query and key lengths (Hq=32, Hkv=4, d=128)")
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the first ten or so steps of a process run slower while the clocks settle
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--B", type=int, default=2)
     ap.add_argument("--N", type=int, default=8192)
     ap.add_argument("--H", type=int, default=16)
     ap.add_argument("--Hkv", type=int, default=0)
     ap.add_argument("--d", type=int, default=128)
     ap.add_argument("--non-causal", action="store_true")
-    ap.add_argument("--dq-mode", type=int, default=0, choices=(0, 1, 2, 3),
+    ap.add_argument("--dq-mode", type=int, default=4, choices=(0, 1, 2, 3, 4),
                     help="dQ reduction: 0 fp32 atomics, 1 semaphore-ordered, 2 partial tiles "
                          "summed by a second kernel, 3 partial tiles summed by the last "
-                         "contributor")
+                         "contributor, 4 int32 fixed-point atomics")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
     ap.add_argument("--traffic-file", default=TRAFFIC_FILE,
@@ -650,7 +659,8 @@ def main():
                          "(extras fwd_<variant>_kernel_ms)")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per measured workload (MHA 2K, headline, 16K/32K, "
-                         "GQA/MQA, packed batch; atomic and ordered dQ; tile-order ablation)")
+                         "GQA/MQA, packed batch; fp32 atomic, ordered and fixed-point dQ; "
+                         "tile-order ablation)")
     ap.add_argument("--sweep-ids", default="",
                     help="with --sweep: only these workload ids, comma-separated "
                          "(C1, H, C2, C3, C4)")
@@ -745,8 +755,8 @@ def main():
         "bwd_tflops": f_bwd / ((ms_bwd + ms_pre + ms_post) / max(1, n_bwd) * 1e-3) / 1e12,
         "pct_of_peak": 100.0 * value / MFMA_BF16_PEAK_TFLOPS,
     }
-    if det == 0:
-        # the fast mode's dQ reduction: device-scope fp32 atomic adds; the
+    if det in (0, 4):
+        # the atomic modes' dQ reduction: device-scope fp32 (int32) atomic adds; the
         # rate they imply over the kernel's time, against what they sustain
         # alone (--atomic-probe), shows how close the kernel is to that bound
         dq_bytes = dq_reduction_bytes(B, N, Hq, d, causal)
@@ -755,8 +765,8 @@ def main():
     if args.extra:
         o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, softmax_scale=scale)
         this_ms = (ms_bwd + ms_pre + ms_post) / max(1, n_bwd)
-        for mode in (0, 1, 2, 3):
-            if mode == det or (d == 256 and mode >= 2):  # partial-tile modes take d <= 128
+        for mode in (0, 1, 2, 3, 4):
+            if mode == det or (d == 256 and mode in (2, 3)):  # partial tiles take d <= 128
                 continue
             wsd = fa.bwd_workspace(x["q"], x["k"], causal, mode)
             for _ in range(3):
@@ -846,7 +856,7 @@ def main():
         "config": {
             "workload": f"{'causal' if causal else 'non-causal'} self-attention forward+backward, "
                         f"B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}, "
-                        f"{('atomic', 'semaphore-ordered', 'partial-tile', 'fused partial-tile')[det]} "
+                        f"{DQ_MODE_NAMES[det]} "
                         f"dQ reduction",
             "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
             "deterministic": det,

@@ -192,9 +192,12 @@ FwdLayout fwd_layout(bool varlen, int nseq, long T, long Tk, int Hq, int d) {
   return l;
 }
 
+// dQ modes whose partial tiles replace the accumulator (dense only)
+bool partial_tile_mode(int m) { return m == fa::kDqPartial || m == fa::kDqFused; }
+
 struct BwdLayout {
   size_t hdr = 0, dvec = 0, lse2 = 0, dq_acc = 0, dq_part = 0, sem = 0, tiles = 0, dk_part = 0,
-         dv_part = 0, total = 0;
+         dv_part = 0, kv_part = 0, kvb = 0, dq_exp = 0, total = 0;
   long head_pairs = 0;  // mode 2: partial dQ tiles per (batch, query head)
   long sem_count = 0;
   int sem_slots = 0;  // varlen: per head
@@ -233,7 +236,7 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, long Tk, int H
   l.lse2 = off;
   off += align_up((size_t)T * Hq * 4);
   l.dq_acc = off;
-  if (deterministic >= 2) {
+  if (partial_tile_mode(deterministic)) {
     l.head_pairs = fa::bwd_partial_pairs(N, causal);
     l.dq_part = off;
     off += align_up((size_t)B * Hq * l.head_pairs * fa::kBwdBQ * d * 4);
@@ -260,6 +263,14 @@ BwdLayout bwd_layout(bool varlen, int B, int N, int nseq, long T, long Tk, int H
     off += align_up((size_t)l.S * Tk * Hkv * d * 4);
     l.dv_part = off;
     off += align_up((size_t)l.S * Tk * Hkv * d * 4);
+  }
+  if (deterministic == fa::kDqFixed) {
+    l.kv_part = off;
+    off += align_up((size_t)Hkv * cdiv(Tk, fa::kKvBoundRows) * 2 * 4);
+    l.kvb = off;
+    off += align_up((size_t)Hkv * 4);
+    l.dq_exp = off;
+    off += align_up((size_t)T * Hq * 4);
   }
   l.total = off;
   return l;
@@ -417,11 +428,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     return st;
   if ((st = check_dims(T, Hq, Hkv, d, causal, scale))) return st;
   if ((st = check_dims(Tk, Hq, Hkv, d, causal, scale))) return st;
-  if (deterministic < 0 || deterministic > 3)
-    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1, 2 or 3");
-  if (varlen && deterministic >= 2)
+  if (deterministic < 0 || deterministic > 4)
+    return fail(FA_ERR_INVALID_ARG, "deterministic must be 0, 1, 2, 3 or 4");
+  if (varlen && partial_tile_mode(deterministic))
     return fail(FA_ERR_UNSUPPORTED, "deterministic == 2 or 3 (partial-tile dQ) is dense-only");
-  if (deterministic >= 2 && !fa::bwd_partial_modes(d))
+  if (partial_tile_mode(deterministic) && !fa::bwd_partial_modes(d))
     return fail(FA_ERR_UNSUPPORTED,
                 "deterministic == 2 or 3 (partial-tile dQ) needs d <= 128 and 32 keys per wave");
   const BwdLayout lay =
@@ -435,14 +446,22 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(at(ws, 0));
   float* dvec = reinterpret_cast<float*>(at(ws, lay.dvec));
-  float* dq_acc = deterministic >= 2 ? nullptr : reinterpret_cast<float*>(at(ws, lay.dq_acc));
+  float* dq_acc =
+      partial_tile_mode(deterministic) ? nullptr : reinterpret_cast<float*>(at(ws, lay.dq_acc));
   int* sem = reinterpret_cast<int*>(at(ws, lay.sem));
+  const bool fixed = deterministic == fa::kDqFixed;
+  float* kvb = fixed ? reinterpret_cast<float*>(at(ws, lay.kvb)) : nullptr;
+  int* dq_exp = fixed ? reinterpret_cast<int*>(at(ws, lay.dq_exp)) : nullptr;
   long tk = timing_start(2, s);
+  hipError_t e = hipSuccess;
+  if (fixed)
+    e = fa::launch_bwd_kv_bound(static_cast<const fa::bf16*>(k), static_cast<const fa::bf16*>(v),
+                                reinterpret_cast<float*>(at(ws, lay.kv_part)), kvb, Tk, Hkv, d, s);
   float* lse2 = reinterpret_cast<float*>(at(ws, lay.lse2));
-  hipError_t e = fa::launch_bwd_pre(static_cast<const fa::bf16*>(o),
-                                    static_cast<const fa::bf16*>(dout), lse, dvec, lse2, dq_acc,
-                                    sem, lay.sem_count, hdr, (int)(T * Hq), Hq, d, varlen, N,
-                                    (int)T, s);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_pre(static_cast<const fa::bf16*>(o), static_cast<const fa::bf16*>(dout),
+                           lse, dvec, lse2, dq_acc, sem, lay.sem_count, hdr, (int)(T * Hq), Hq, d,
+                           varlen, N, (int)T, kvb, Hq / Hkv, dq_exp, s);
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
 
@@ -454,12 +473,14 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   p.lse = lse2;  // LSE * log2(e), written by the preprocess
   p.dvec = dvec;
   p.dq_acc = dq_acc;
+  p.dq_exp = dq_exp;
   p.dk = static_cast<fa::bf16*>(dk);
   p.dv = static_cast<fa::bf16*>(dv);
   p.dk_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dk_part)) : nullptr;
   p.dv_part = lay.S > 1 ? reinterpret_cast<float*>(at(ws, lay.dv_part)) : nullptr;
   p.sem = sem;
-  p.dq_part = deterministic >= 2 ? reinterpret_cast<float*>(at(ws, lay.dq_part)) : nullptr;
+  p.dq_part =
+      partial_tile_mode(deterministic) ? reinterpret_cast<float*>(at(ws, lay.dq_part)) : nullptr;
   p.dq = static_cast<fa::bf16*>(dq);
   p.head_pairs = lay.head_pairs;
   p.hdr = hdr;
@@ -481,7 +502,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     int* tiles = reinterpret_cast<int*>(at(ws, lay.tiles));
     tk = timing_start(4, s);
     e = fa::launch_sched(cu, cu_k, nseq, (int)T, (int)Tk, fa::bwd_tile_keys(d),
-                         deterministic ? 2 : 1,
+                         deterministic == fa::kDqOrdered ? 2 : 1,
                          causal != 0, fa::fwd_tile_keys(), fa::kBwdBQ, tiles, lay.max_tiles,
                          nullptr, 0, hdr, p.sched == 0, s);
     timing_stop(tk, s);
@@ -509,18 +530,18 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     if (lay.S > 1)
       e = fa::launch_bwd_post(nullptr, nullptr, 0, scale, p.dk_part, p.dv_part,
                               static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
-                              Tk * Hkv * d, lay.S, s);
+                              Tk * Hkv * d, lay.S, nullptr, d, s);
   } else if (deterministic == 2) {
     e = fa::launch_bwd_dq_reduce(p.dq_part, static_cast<fa::bf16*>(dq), B, N, Hq, d, causal != 0,
                                  p.nq, p.nkv, lay.head_pairs, scale, s);
     if (e == hipSuccess && lay.S > 1)
       e = fa::launch_bwd_post(nullptr, nullptr, 0, scale, p.dk_part, p.dv_part,
                               static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
-                              Tk * Hkv * d, lay.S, s);
+                              Tk * Hkv * d, lay.S, nullptr, d, s);
   } else {
     e = fa::launch_bwd_post(dq_acc, static_cast<fa::bf16*>(dq), T * Hq * d, scale, p.dk_part,
                             p.dv_part, static_cast<fa::bf16*>(dk), static_cast<fa::bf16*>(dv),
-                            Tk * Hkv * d, lay.S, s);
+                            Tk * Hkv * d, lay.S, dq_exp, d, s);
   }
   timing_stop(tk, s);
   if (e != hipSuccess) return hip_fail(e, "backward post launch");
@@ -575,8 +596,8 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic) {
   if (!dense_ok(B, N) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
-  if (deterministic < 0 || deterministic > 3) return 0;
-  if (deterministic >= 2 && !fa::bwd_partial_modes(d)) return 0;
+  if (deterministic < 0 || deterministic > 4) return 0;
+  if (partial_tile_mode(deterministic) && !fa::bwd_partial_modes(d)) return 0;
   return bwd_layout(false, B, N, 0, (long)B * N, (long)B * N, Hq, Hkv, d, deterministic,
                     causal != 0).total;
 }
@@ -612,7 +633,7 @@ size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv,
                                     int causal, int deterministic) {
   (void)causal;
   if (nseq <= 0 || total_tokens <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
-  if (deterministic < 0 || deterministic > 1) return 0;
+  if (deterministic < 0 || deterministic > 4 || partial_tile_mode(deterministic)) return 0;
   return bwd_layout(true, 0, 0, nseq, total_tokens, total_tokens, Hq, Hkv, d, deterministic,
                     causal != 0).total;
 }
@@ -693,7 +714,7 @@ int fa_varlen_qk_fwd_fp8(const void* q8, const void* k8, const void* v, void* o,
 size_t fa_varlen_qk_bwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
                                        int d, int causal, int deterministic) {
   if (nseq <= 0 || total_q <= 0 || total_k <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
-  if (deterministic < 0 || deterministic > 1) return 0;
+  if (deterministic < 0 || deterministic > 4 || partial_tile_mode(deterministic)) return 0;
   return bwd_layout(true, 0, 0, nseq, total_q, total_k, Hq, Hkv, d, deterministic, causal != 0)
       .total;
 }
@@ -721,10 +742,10 @@ int fa_probe_dq_reduction(float* buf, int rows, int row_floats, int blocks, int 
     return fail(FA_ERR_INVALID_ARG, "row_floats must be a positive multiple of 128");
   if ((long)row_floats * 32 * 4 >= (1L << 31)) return fail(FA_ERR_UNSUPPORTED, "rows too wide");
   if (blocks <= 0 || items <= 0) return fail(FA_ERR_INVALID_ARG, "blocks and items must be positive");
-  if (store != 0 && store != 1) return fail(FA_ERR_INVALID_ARG, "store must be 0 or 1");
+  if (store < 0 || store > 2) return fail(FA_ERR_INVALID_ARG, "store must be 0, 1 or 2");
   std::string why;
   if ((st = check_device(&why))) return fail(st, why);
-  hipError_t e = fa::launch_probe_dq(buf, rows, row_floats, blocks, items, store != 0,
+  hipError_t e = fa::launch_probe_dq(buf, rows, row_floats, blocks, items, store,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   return FA_OK;

@@ -2,7 +2,8 @@
 //
 // Method ([FA2] "Core method" 2 and 4; [FA4B] 2.1, 3.2, 3.3.1, 5.2, 5.3):
 //  * preprocess: D = rowsum(dO o O) per query row (fp32), and the fp32 dQ
-//    accumulator, the ordering semaphores and the workspace header are zeroed;
+//    accumulator, the ordering semaphores and the workspace header are zeroed
+//    (fixed-point mode: also each row's fixed-point exponent);
 //  * main kernel: one workgroup per (sequence, key/value head, key tile of 256
 //    keys -- 128 for d = 256, with one workgroup per half of the output
 //    columns --, query-head subgroup).  Each of the 8 (d = 256: 4) waves owns
@@ -29,9 +30,15 @@
 //    query tile's partial tiles in ascending key-tile order, or (fused) each
 //    workgroup counts itself in with one atomic per tile once its stores are
 //    complete and the last contributor of a query tile does that sum and
-//    writes bf16 dQ itself.
-//  * post: dQ = bf16(scale * dQ_acc); split subgroups' dK/dV partials are
-//    summed in a fixed order.
+//    writes bf16 dQ itself.  The fixed-point mode adds with int32 device
+//    atomics, which this GPU performs faster than fp32 ones: every
+//    contribution to row i is rounded to a multiple of 2^-e_i, with e_i set
+//    from a bound on the row's dQ (|dO_i| times the largest V row norm and
+//    the largest |K| element of the key/value head, which a scan of K and V
+//    before the preprocess finds) so that the int32 sums cannot overflow;
+//    integer adds are exact, so the result does not depend on their order.
+//  * post: dQ = bf16(scale * dQ_acc) (fixed point: scaled by 2^-e_i first);
+//    split subgroups' dK/dV partials are summed in a fixed order.
 // A packed sequence may have Lq queries and Lk keys (the decode-shaped
 // batches of [FA4B] 3.3.2): the causal diagonal is then aligned bottom-right
 // (query i sees key j iff j <= i + Lk - Lq), the walk of a key tile starts at
@@ -110,6 +117,7 @@ __global__ __launch_bounds__(bwd_threads(D)) void bwd_kernel(BwdParams p) {
   constexpr int DH = D / NHALF;     // output columns per workgroup
   constexpr bool DET = DQM == kDqOrdered;
   constexpr bool FUSED = DQM == kDqFused;
+  constexpr bool FIXED = DQM == kDqFixed;
   constexpr bool PARTS = DQM == kDqPartial || FUSED;  // partial tiles in dq_part
   using L = BwdLds<D>;
   constexpr int ST = L::STRIDE;
@@ -127,6 +135,10 @@ __global__ __launch_bounds__(bwd_threads(D)) void bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char ds_s1[L::dsBytes];
   __shared__ int sh_ticket;
   __shared__ int sh_last[4];  // fused mode: "this workgroup completes item t" (t mod 4)
+  // fixed-point mode: the query tile's row exponents, item t in slot t mod 3
+  // (copied with item t's rows, read by item t's dQ adds one item later,
+  // while item t+2's copy goes to the third slot)
+  __shared__ __attribute__((aligned(16))) int ex_s[FIXED ? 3 : 1][BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -277,6 +289,10 @@ __global__ __launch_bounds__(bwd_threads(D)) void bwd_kernel(BwdParams p) {
       const int q = min(q0 + l32, qlast);
       if (half == 0) dma4(p.lse + base + q, std_);
       else dma4(p.dvec + base + q, std_);
+    }
+    if (FIXED && wave == NW - 2 && half == 0) {
+      const int q = min(q0 + l32, qlast);
+      dma4(p.dq_exp + (tok - q0 + q) * p.Hq + h, ex_s[item % 3]);
     }
   };
 
@@ -429,6 +445,23 @@ __global__ __launch_bounds__(bwd_threads(D)) void bwd_kernel(BwdParams p) {
       int vo = ((16 * qb0 + 4 * g16) * (int)q_row + dh0 + dblk * 16 + L16) * 4;
       asm volatile("" : "+v"(vo));
       const int row_bytes = (int)q_row * 4;
+      if (FIXED) {
+        // round(x 2^e) of row q, added as int32: exact, so the order of the
+        // adds does not matter
+        const int* ex = ex_s[item % 3];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const i32x4 ev = *reinterpret_cast<const i32x4*>(ex + 16 * (qb0 + qb) + 4 * g16);
+#pragma unroll
+          for (int c = 0; c < NCB; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+                  __float2int_rn(__builtin_amdgcn_ldexpf(acc[c * NQB + qb][r], ev[r])), rsrc,
+                  vo + (16 * qb + r) * row_bytes + 64 * c, 0, 0);
+        }
+        return;
+      }
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -750,7 +783,7 @@ __global__ __launch_bounds__(bwd_threads(D)) void bwd_kernel(BwdParams p) {
   // or stores of the dQ issued in the previous item (4 NQB or NQB per wave)
   // were issued after them, so those stay in flight.
   auto wait_copies = [&](int item) {
-    if ((DQM == kDqAtomic || DET) && item >= 2) wait_vmem_leave<4 * NQB * NCB>();
+    if ((DQM == kDqAtomic || DET || FIXED) && item >= 2) wait_vmem_leave<4 * NQB * NCB>();
     else if (PARTS && item >= 2) wait_vmem_leave<NQB>();
     else wait_vmem();
     lds_barrier();
@@ -841,6 +874,7 @@ hipError_t launch_bwd_t(const BwdParams& p, int grid, hipStream_t stream) {
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_mode(const BwdParams& p, int mode, int grid, hipStream_t stream) {
   if (mode == kDqOrdered) return launch_bwd_t<D, CAUSAL, VARLEN, kDqOrdered>(p, grid, stream);
+  if (mode == kDqFixed) return launch_bwd_t<D, CAUSAL, VARLEN, kDqFixed>(p, grid, stream);
   if constexpr (D != 256 && bwd_key_blocks(D) == 1) {  // partial tiles: 32 keys per wave
     if (mode == kDqPartial && !VARLEN)
       return launch_bwd_t<D, CAUSAL, false, kDqPartial>(p, grid, stream);
@@ -867,7 +901,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
                                                       const float* lse, float* dvec, float* lse2,
                                                       float* dq_acc, int* sem, long sem_count,
                                                       uint32_t* hdr, int rows, int Hq, bool varlen,
-                                                      int N, int T) {
+                                                      int N, int T, const float* kvb, int G,
+                                                      int* dq_exp) {
   constexpr int EPT = D / 16;  // elements per thread (16 threads per row)
   // a block takes 16 consecutive tokens of one query head, so that its D
   // and LSE values are 16 consecutive floats of their [b, h, n] arrays
@@ -880,20 +915,44 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
     sem[s] = 0;
   if (tok >= rows / Hq) return;
   const long base = (long)row * D + sub * EPT;
-  float acc = 0.f;
+  float acc = 0.f, nrm = 0.f;  // D and |dO|^2 of the row
   if (EPT == 8) {
     const u32x4 a = ld_global16(o + base), b = ld_global16(dout + base);
     const bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    for (int e = 0; e < 8; ++e) {
+      acc = fmaf((float)x[e], (float)y[e], acc);
+      nrm = fmaf((float)y[e], (float)y[e], nrm);
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) acc = fmaf((float)o[base + e], (float)dout[base + e], acc);
+    for (int e = 0; e < EPT; ++e) {
+      acc = fmaf((float)o[base + e], (float)dout[base + e], acc);
+      nrm = fmaf((float)dout[base + e], (float)dout[base + e], nrm);
+    }
   }
   acc += __shfl_xor(acc, 8, 16);
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
+  if (dq_exp) {
+    nrm += __shfl_xor(nrm, 8, 16);
+    nrm += __shfl_xor(nrm, 4, 16);
+    nrm += __shfl_xor(nrm, 2, 16);
+    nrm += __shfl_xor(nrm, 1, 16);
+    // beta = |dO| max|K| max|V| bounds every element of the row's unscaled
+    // dQ, and every partial sum of it over a subset of the keys:
+    // |sum_j P_j (dP_j - D) K_jc| <= max|K| sum_j P_j |dP_j - D|, the mean
+    // absolute deviation of dP_j = dO . V_j under the weights P_j around their
+    // mean D, which is at most their standard deviation, which is at most half
+    // their range (Popoviciu), <= |dO| max|V|.  beta < 2^k, so the sums stay
+    // below 2^29 steps of 2^(k - 29), with 4x headroom in int32 for the
+    // rounding of P, D and dS.
+    const float beta = sqrtf(nrm) * kvb[h / G];
+    int ex = kDqFixedBits - __builtin_amdgcn_frexp_expf(beta);
+    if (!(beta <= 3.0e38f)) ex = kDqExpNonFinite;
+    if (sub == 0) dq_exp[row] = ex;
+  }
   if (dq_acc) {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -913,14 +972,110 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
   }
 }
 
+// ---------------------------------------------------------------------------
+// fixed-point dQ: the K/V magnitudes of each key/value head.  Partial maxima
+// per kKvBoundRows key rows (largest |K| element, largest squared V row norm),
+// then one workgroup per head combines them.  NaN propagates through both
+// maxima (a NaN input gives a non-finite bound, hence NaN dQ rows).
+__device__ __forceinline__ float max_nan(float a, float b) { return (a > b || a != a) ? a : b; }
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kv_bound_kernel(const bf16* k, const bf16* v,
+                                                           float* part, long Tk, int Hkv,
+                                                           int nchunk) {
+  constexpr int TPR = D / 8;      // threads per key row, 8 elements each
+  constexpr int RPP = 256 / TPR;  // rows per pass
+  __shared__ float red[2][4];
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int sub = threadIdx.x % TPR;
+  float km = 0.f, vm = 0.f;
+  for (int r = threadIdx.x / TPR; r < kKvBoundRows; r += RPP) {
+    const long row = (long)chunk * kKvBoundRows + r;
+    float ss = 0.f;
+    if (row < Tk) {
+      const long base = (row * Hkv + g) * D + sub * 8;
+      const bf16x8 a = as_bf16x8(ld_global16(k + base)), b = as_bf16x8(ld_global16(v + base));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        km = max_nan(fabsf((float)a[e]), km);
+        ss = fmaf((float)b[e], (float)b[e], ss);
+      }
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
+    vm = max_nan(ss, vm);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    km = max_nan(__shfl_xor(km, m), km);
+    vm = max_nan(__shfl_xor(vm, m), vm);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = km;
+    red[1][wave] = vm;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      km = max_nan(red[0][w], km);
+      vm = max_nan(red[1][w], vm);
+    }
+    part[2 * ((long)g * nchunk + chunk)] = km;
+    part[2 * ((long)g * nchunk + chunk) + 1] = sqrtf(vm);
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* part, float* kvb,
+                                                            int nchunk) {
+  __shared__ float red[2][4];
+  const int g = blockIdx.x;
+  float km = 0.f, vm = 0.f;
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    km = max_nan(part[2 * ((long)g * nchunk + c)], km);
+    vm = max_nan(part[2 * ((long)g * nchunk + c) + 1], vm);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    km = max_nan(__shfl_xor(km, m), km);
+    vm = max_nan(__shfl_xor(vm, m), vm);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = km;
+    red[1][wave] = vm;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      km = max_nan(red[0][w], km);
+      vm = max_nan(red[1][w], vm);
+    }
+    kvb[g] = km * vm;
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_post_kernel(const float* dq_acc, bf16* dq, long dq_vec,
                                                        float scale, const float* dk_part,
                                                        const float* dv_part, bf16* dk, bf16* dv,
-                                                       long kv_vec, int S) {
+                                                       long kv_vec, int S, const int* dq_exp,
+                                                       int row_vec_shift) {
   // every element handled in groups of 4 (all sizes are multiples of 64)
   const long stride = (long)gridDim.x * 256;
   for (long v = (long)blockIdx.x * 256 + threadIdx.x; v < dq_vec; v += stride) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(dq_acc + 4 * v);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(dq_acc + 4 * v);
+    f32x4 a;
+    if (dq_exp) {
+      // int32 fixed point of row v / (d / 4), in units of 2^-e
+      const int ex = dq_exp[v >> row_vec_shift];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a[e] = ex == kDqExpNonFinite ? __builtin_nanf("")
+                                     : __builtin_amdgcn_ldexpf((float)(int)raw[e], -ex);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = __uint_as_float(raw[e]);
+    }
     u32x2 w;
     w[0] = pack2_bf16(a[0] * scale, a[1] * scale);
     w[1] = pack2_bf16(a[2] * scale, a[3] * scale);
@@ -1024,9 +1179,10 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* part, b
 // its products.  Workgroup w of 8 waves, at step t, takes the 32-row x 128-
 // column tile ((w + t * gridDim.x) mod tiles) of a [rows, row_floats] fp32
 // buffer; wave v adds its 32 x 16 column block with the 8 buffer atomic
-// instructions (4 rows x 16 columns each) the backward issues per item, or,
-// with STORE, writes the same bytes with plain stores.
-template <bool STORE>
+// instructions (4 rows x 16 columns each) the backward issues per item, or
+// (KIND 1) writes the same bytes with plain stores, or (KIND 2) adds the
+// int32 1 with the fixed-point mode's int32 atomics.
+template <int KIND>
 __global__ __launch_bounds__(512) void probe_dq_kernel(float* buf, int rows, int row_floats,
                                                         int items) {
   const int lane = threadIdx.x & 63;
@@ -1047,8 +1203,10 @@ __global__ __launch_bounds__(512) void probe_dq_kernel(float* buf, int rows, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int off = vo + (16 * qb + r) * row_floats * 4;
-        if (STORE)
+        if (KIND == 1)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), rsrc, off, 0, 0);
+        else if (KIND == 2)
+          (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, rsrc, off, 0, 0);
         else
           (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(val, rsrc, off, 0, 0);
       }
@@ -1057,13 +1215,16 @@ __global__ __launch_bounds__(512) void probe_dq_kernel(float* buf, int rows, int
 
 }  // namespace
 
-hipError_t launch_probe_dq(float* buf, int rows, int row_floats, int blocks, int items, bool store,
+hipError_t launch_probe_dq(float* buf, int rows, int row_floats, int blocks, int items, int kind,
                            hipStream_t stream) {
-  if (store)
-    hipLaunchKernelGGL(probe_dq_kernel<true>, dim3(blocks), dim3(512), 0, stream, buf, rows,
+  if (kind == 1)
+    hipLaunchKernelGGL(probe_dq_kernel<1>, dim3(blocks), dim3(512), 0, stream, buf, rows,
+                       row_floats, items);
+  else if (kind == 2)
+    hipLaunchKernelGGL(probe_dq_kernel<2>, dim3(blocks), dim3(512), 0, stream, buf, rows,
                        row_floats, items);
   else
-    hipLaunchKernelGGL(probe_dq_kernel<false>, dim3(blocks), dim3(512), 0, stream, buf, rows,
+    hipLaunchKernelGGL(probe_dq_kernel<0>, dim3(blocks), dim3(512), 0, stream, buf, rows,
                        row_floats, items);
   return hipGetLastError();
 }
@@ -1108,28 +1269,50 @@ long bwd_partial_pairs(int N, bool causal) {
 
 hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, float* dvec,
                           float* lse2, float* dq_acc, int* sem, long sem_count, uint32_t* hdr,
-                          int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream) {
+                          int rows, int Hq, int d, bool varlen, int N, int T, const float* kvb,
+                          int G, int* dq_exp, hipStream_t stream) {
   const int grid = max(1, Hq * ((rows / Hq + 15) / 16));
   if (d == 256)
     hipLaunchKernelGGL(bwd_pre_kernel<256>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
-                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
+                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T, kvb, G, dq_exp);
   else if (d == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
-                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
+                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T, kvb, G, dq_exp);
   else
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid), dim3(256), 0, stream, o, dout, lse, dvec,
-                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T);
+                       lse2, dq_acc, sem, sem_count, hdr, rows, Hq, varlen, N, T, kvb, G, dq_exp);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv_bound(const bf16* k, const bf16* v, float* part, float* kvb, long Tk,
+                               int Hkv, int d, hipStream_t stream) {
+  const int nchunk = (int)((Tk + kKvBoundRows - 1) / kKvBoundRows);
+  if (nchunk > 0) {
+    const dim3 grid(nchunk, Hkv);
+    if (d == 256)
+      hipLaunchKernelGGL(bwd_kv_bound_kernel<256>, grid, dim3(256), 0, stream, k, v, part, Tk,
+                         Hkv, nchunk);
+    else if (d == 128)
+      hipLaunchKernelGGL(bwd_kv_bound_kernel<128>, grid, dim3(256), 0, stream, k, v, part, Tk,
+                         Hkv, nchunk);
+    else
+      hipLaunchKernelGGL(bwd_kv_bound_kernel<64>, grid, dim3(256), 0, stream, k, v, part, Tk,
+                         Hkv, nchunk);
+  }
+  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(Hkv), dim3(256), 0, stream, part, kvb, nchunk);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float scale,
                            const float* dk_part, const float* dv_part, bf16* dk, bf16* dv,
-                           long kv_elems, int S, hipStream_t stream) {
+                           long kv_elems, int S, const int* dq_exp, int d, hipStream_t stream) {
   const long vec = dq_elems / 4;
   const long work = max(vec, S > 1 ? kv_elems / 4 : 0L);
   const long blocks = min(4096L, max(1L, (work + 255) / 256));
+  const int row_vec_shift = d == 256 ? 6 : (d == 128 ? 5 : 4);  // log2(d / 4)
   hipLaunchKernelGGL(bwd_post_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dq_acc, dq,
-                     vec, scale, dk_part, dv_part, dk, dv, kv_elems / 4, S);
+                     vec, scale, dk_part, dv_part, dk, dv, kv_elems / 4, S, dq_exp,
+                     row_vec_shift);
   return hipGetLastError();
 }
 

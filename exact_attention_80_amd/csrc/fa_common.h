@@ -467,7 +467,8 @@ struct BwdParams {
   const bf16* dout;
   const float* lse;       // LSE * log2(e), laid out like the forward's logsumexp
   const float* dvec;      // D = rowsum(dO o O), laid out like lse
-  float* dq_acc;          // [T, Hq, d] fp32
+  float* dq_acc;          // [T, Hq, d] fp32 (int32 fixed point in the fixed-point mode)
+  const int* dq_exp;      // fixed-point mode: [T, Hq] exponent of each row's fixed-point scale
   bf16* dk;
   bf16* dv;
   float* dk_part;         // [S, Tk, Hkv, d] fp32 when S > 1

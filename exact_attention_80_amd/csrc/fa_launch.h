@@ -31,6 +31,17 @@ constexpr int kDqAtomic = 0;   // fp32 device atomics into dq_acc
 constexpr int kDqOrdered = 1;  // semaphore-ordered adds into dq_acc (bit-reproducible)
 constexpr int kDqPartial = 2;  // plain stores of every partial tile, summed by bwd_dq_reduce
 constexpr int kDqFused = 3;    // partial tiles summed by the last workgroup to finish its own
+constexpr int kDqFixed = 4;    // int32 fixed-point device atomics (bit-reproducible)
+
+// Fixed-point dQ: row i of a query head accumulates round(x 2^e_i) in int32,
+// where e_i = kDqFixedBits - (binary exponent of beta_i) and
+// beta_i = |dO_i| max_j |V_j| max_jc |K_jc| bounds every element of the row's
+// unscaled dQ and every partial sum of it, so the sum stays below
+// 2^kDqFixedBits (2 bits of headroom in int32) and the integer adds are exact
+// in any order.  kDqExpNonFinite marks a row whose bound is not finite.
+constexpr int kDqFixedBits = 29;
+constexpr int kDqExpNonFinite = 1 << 20;
+constexpr int kKvBoundRows = 256;  // key rows per partial of the K/V magnitude scan
 
 // Index of the partial dQ tile of (query tile i, key tile j) inside its
 // (sequence, head): the query tiles' key-tile counts laid end to end (causal:
@@ -58,14 +69,24 @@ hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool varlen, i
 
 // D = rowsum(dO o O) and LSE * log2(e) in the logsumexp layout; zeroes the
 // fp32 dQ accumulator (when given), the semaphores and the workspace header.
+// With kvb (fixed-point mode) it also writes each row's fixed-point exponent
+// to dq_exp ([T, Hq]) from |dO_i| and kvb[h / G].
 hipError_t launch_bwd_pre(const bf16* o, const bf16* dout, const float* lse, float* dvec,
                           float* lse2, float* dq_acc, int* sem, long sem_count, uint32_t* hdr,
-                          int rows, int Hq, int d, bool varlen, int N, int T, hipStream_t stream);
+                          int rows, int Hq, int d, bool varlen, int N, int T, const float* kvb,
+                          int G, int* dq_exp, hipStream_t stream);
+
+// Fixed-point mode, before the preprocess: kvb[g] = max_jc |K_jc| * max_j |V_j|
+// over every key row j of key/value head g (Tk rows of [Tk, Hkv, d]); part
+// holds Hkv * ceil(Tk / kKvBoundRows) pairs of partial maxima.  Non-finite
+// values propagate.
+hipError_t launch_bwd_kv_bound(const bf16* k, const bf16* v, float* part, float* kvb, long Tk,
+                               int Hkv, int d, hipStream_t stream);
 
 // mode: dQ reduction across key tiles (0 fp32 atomics, 1 semaphore-ordered
 // adds, 2 partial tiles summed by launch_bwd_dq_reduce, 3 partial tiles summed
-// inside the kernel by the last contributor of each query tile; 2 and 3 are
-// dense-only)
+// inside the kernel by the last contributor of each query tile, 4 int32
+// fixed-point atomics; 2 and 3 are dense-only)
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, int mode, int grid,
                       hipStream_t stream);
 
@@ -81,14 +102,17 @@ long bwd_partial_pairs(int N, bool causal);
 bool bwd_partial_modes(int d);
 
 // dQ = bf16(scale * dQ_acc); when S > 1 also dK/dV = bf16(sum of the S partials).
-// dq_elems counts query-side elements, kv_elems key-side ones.
+// dq_elems counts query-side elements, kv_elems key-side ones.  With dq_exp
+// (fixed-point mode) dQ_acc holds int32 values of row r (of d elements) in
+// units of 2^-dq_exp[r].
 hipError_t launch_bwd_post(const float* dq_acc, bf16* dq, long dq_elems, float scale,
                            const float* dk_part, const float* dv_part, bf16* dk, bf16* dv,
-                           long kv_elems, int S, hipStream_t stream);
+                           long kv_elems, int S, const int* dq_exp, int d, hipStream_t stream);
 
 // Measurement aid (fa_probe_dq_reduction): the backward's atomic dQ reduction
-// pattern alone, or the same bytes as plain stores.
-hipError_t launch_probe_dq(float* buf, int rows, int row_floats, int blocks, int items, bool store,
+// pattern alone (kind 0 fp32 adds, 2 int32 adds), or the same bytes as plain
+// stores (kind 1).
+hipError_t launch_probe_dq(float* buf, int rows, int row_floats, int blocks, int items, int kind,
                            hipStream_t stream);
 
 // Variable-length scheduler: validates the query and key offsets (cu_q and

@@ -183,8 +183,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
     deterministic selects the dQ reduction across key tiles: 0 (False) fp32
     atomics, 1 (True) semaphore-ordered adds, 2 partial tiles summed in a fixed
     order by a second kernel, 3 partial tiles summed in a fixed order by the
-    last workgroup to contribute to each query tile; 1, 2 and 3 are
-    bit-reproducible.  Mode 1 bounds its waits: one that expires leaves dQ
+    last workgroup to contribute to each query tile, 4 int32 fixed-point
+    atomics (per-row scale from a bound on the row's dQ; exact sums in any
+    order, the fastest mode); 1 to 4 are bit-reproducible.  Mode 1 bounds its waits: one that expires leaves dQ
     correct but unordered and sets a bit that workspace_error(workspace)
     reports (check it after the call when reproducibility matters).  lib:
     another build of the library (load_variant), default this package's."""
@@ -255,8 +256,8 @@ def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, softmax_scale: float |
 def varlen_bwd(q, k, v, o, lse, do, cu_seqlens, causal: bool = False,
                softmax_scale: float | None = None, deterministic: bool = False,
                max_seqlen: int = 0, workspace: torch.Tensor | None = None, lib=None):
-    """Packed backward -> (dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d]).  lib: another
-    build of the library (load_variant)."""
+    """Packed backward -> (dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d]); deterministic
+    0, 1 or 4 as in bwd.  lib: another build of the library (load_variant)."""
     L = _lib if lib is None else lib
     T, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -400,7 +401,7 @@ def varlen_qk_bwd(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, causal: bool 
                   max_seqlen_q: int = 0, max_seqlen_k: int = 0,
                   workspace: torch.Tensor | None = None, lib=None):
     """Packed backward with separate query and key lengths
-    -> (dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]); deterministic 0 or 1.
+    -> (dq [Tq,Hq,d], dk [Tk,Hkv,d], dv [Tk,Hkv,d]); deterministic 0, 1 or 4.
     lib: another build of the library (load_variant)."""
     L = _lib if lib is None else lib
     Tq, Hq, d = q.shape
@@ -459,9 +460,11 @@ def timing_end(lib=None) -> dict:
     return {k: (int(counts[i]), float(ms[i])) for i, k in enumerate(TIMING_KINDS)}
 
 
-def probe_dq_reduction(buf, blocks: int, items: int, store: bool = False) -> int:
+def probe_dq_reduction(buf, blocks: int, items: int, store: int | bool = False) -> int:
     """Launch the dQ-reduction measurement kernel on buf [rows, row_floats]
-    fp32 (rows % 32 == 0, row_floats % 128 == 0); returns the bytes it moves."""
+    fp32 (rows % 32 == 0, row_floats % 128 == 0): store 0 (False) fp32 atomic
+    adds, 1 (True) plain stores, 2 int32 atomic adds (buf holds int32 bits);
+    returns the bytes it moves."""
     _need(buf, "buf", tuple(buf.shape), torch.float32)
     rows, row_floats = buf.shape
     _check(_lib.fa_probe_dq_reduction(buf.data_ptr(), rows, row_floats, blocks, items, int(store),

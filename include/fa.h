@@ -140,7 +140,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
  * for deterministic == 2 or 3, the fp32 partial dQ tiles (32 x d floats per
  * pair of a 32-row query tile and a 256-key tile that meet: about 2.2 GB for
  * causal B=2, Hq=16, N=8192, d=128), ordering semaphores or arrival counters,
- * split dK/dV partials).  0 when the sizes or the mode are invalid. */
+ * split dK/dV partials; for deterministic == 4 an int32 accumulator, the K/V
+ * maxima and one exponent per query row and head).  0 when the sizes or the
+ * mode are invalid. */
 size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
                              int deterministic);
 
@@ -158,10 +160,23 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
  * dense layout only), or, when deterministic == 3, stored the same way
  * (coherent for the whole device) and summed in the same order inside the
  * main kernel by the last workgroup to contribute to each query tile, which
- * writes dQ itself (one counting atomic per tile; dense layout only).
- * Modes 1, 2 and 3 make dQ/dK/dV bit-identical from run to run (and the
- * partial-tile modes 2 and 3 give the same dQ).  dK/dV never use atomics.
- * Any other value: FA_ERR_INVALID_ARG.
+ * writes dQ itself (one counting atomic per tile; dense layout only), or,
+ * when deterministic == 4, added with int32 device atomics in fixed point:
+ * row i of query head h accumulates round(x 2^e) of every contribution x,
+ * where 2^e is the largest power of two that keeps the bound
+ * |dO_i| max_j |V_j| max |K| (K/V maxima over every key row of the key/value
+ * head; a bound on every element of the row's unscaled dQ, see
+ * fa_bwd.hip) below 2^29, so the integer sums are exact and do not depend
+ * on the order of the adds.  A preprocessing pass reads K and V once for
+ * those maxima.  The result differs from the fp32 sum by at most (number of
+ * key tiles) / 2 + 32 steps of 2^-e per element before the final bf16
+ * rounding (a row's dQ has about 29 significant bits relative to its bound);
+ * a row whose bound is not finite (non-finite dO, K or V) gets dQ = NaN.
+ * This is an MI355X-specific choice: int32 device atomics sustain about 1.7
+ * TB/s against 1.35 TB/s for fp32 ones (fa_probe_dq_reduction).
+ * Modes 1 to 4 make dQ/dK/dV bit-identical from run to run (and the
+ * partial-tile modes 2 and 3 give the same dQ); mode 4 also across tile
+ * orders.  dK/dV never use atomics.  Any other value: FA_ERR_INVALID_ARG.
  * Mode 1 bounds every semaphore wait (2 s, or FA_DET_SPIN_TICKS ticks of the
  * 100 MHz clock from the environment); a wait that expires sets
  * FA_DEVERR_WAIT_TIMEOUT in the workspace and the adds proceed unordered, so
@@ -206,7 +221,8 @@ size_t fa_varlen_bwd_workspace_size(int nseq, int total_tokens, int Hq, int Hkv,
                                     int causal, int deterministic);
 
 /* Backward over a packed batch; semantics as fa_bwd, per sequence.
- * deterministic must be 0 or 1 (2 or 3 returns FA_ERR_UNSUPPORTED). */
+ * deterministic must be 0, 1 or 4 (2 or 3 returns FA_ERR_UNSUPPORTED); in
+ * mode 4 the K/V maxima run over every key row of the batch. */
 int fa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
@@ -269,7 +285,7 @@ int fa_varlen_qk_fwd_fp8(const void* q8, const void* k8, const void* v, void* o,
                          int Hkv, int d, float softmax_scale, float q_descale, float k_descale,
                          int causal, void* ws, size_t ws_bytes, void* stream);
 
-/* deterministic must be 0 or 1 (2 or 3 returns FA_ERR_UNSUPPORTED); the size
+/* deterministic must be 0, 1 or 4 (2 or 3 returns FA_ERR_UNSUPPORTED); the size
  * query returns 0 for invalid sizes or modes. */
 size_t fa_varlen_qk_bwd_workspace_size(int nseq, int total_q, int total_k, int Hq, int Hkv,
                                        int d, int causal, int deterministic);
@@ -313,8 +329,10 @@ int fa_workspace_error(const void* ws, size_t ws_bytes, void* stream, uint32_t* 
  * row_floats of 128) and add 1/1024 to every element of the tile with the
  * backward's buffer atomic instructions (32 x 16 columns per wave, 4 rows x
  * 16 columns per instruction), or, with store = 1, write the same bytes with
- * plain stores.  Moves blocks * items * 16 KiB; asynchronous on `stream`;
- * the caller times it. */
+ * plain stores, or, with store = 2, add the int32 1 to every element with the
+ * int32 atomic instructions of the fixed-point dQ mode (deterministic == 4;
+ * buf then holds int32 values).  Moves blocks * items * 16 KiB; asynchronous
+ * on `stream`; the caller times it. */
 int fa_probe_dq_reduction(float* buf, int rows, int row_floats, int blocks, int items, int store,
                           void* stream);
 

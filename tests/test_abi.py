@@ -120,14 +120,15 @@ def bwd(lib, ws=P, ws_bytes=None, det=0, d=64, dq=P, B=1, N=128, Hq=2, Hkv=2):
 def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws_bytes=16) == WORKSPACE
-    assert bwd(lib, det=4) == INVALID
+    assert bwd(lib, det=5, ws_bytes=1 << 30) == INVALID
     assert bwd(lib, det=-1) == INVALID
     assert bwd(lib, dq=None) == INVALID
     assert bwd(lib, d=80) == UNSUPPORTED
     assert bwd(lib, d=512) == UNSUPPORTED
-    # d = 256 takes the atomic and ordered modes only
+    # d = 256 takes the atomic, ordered and fixed-point modes only
     assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 0) > 0
     assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 1) > 0
+    assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 4) > 0
     assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 2) == 0
     assert lib.fa_bwd_workspace_size(1, 128, 2, 2, 256, 1, 3) == 0
     ws2 = lib.fa_bwd_workspace_size(1, 128, 2, 2, 128, 0, 2)
@@ -154,7 +155,12 @@ def test_workspace_sizes(lib):
     # fused partial-sum mode: the same partial tiles plus one counter per query tile
     fused = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 3)
     assert 0 <= fused - part <= B * Hq * nq * 4 + 512
-    assert lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 4) == 0
+    # fixed-point mode: the accumulator (int32) plus the K/V maxima (two floats per
+    # 256 key rows and key/value head, one per head) and one exponent per row
+    fixed = lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 4)
+    extra = Hkv * ((B * N + 255) // 256) * 8 + Hkv * 4 + B * N * Hq * 4
+    assert extra <= fixed - fast <= extra + 3 * 256
+    assert lib.fa_bwd_workspace_size(B, N, Hq, Hkv, d, 1, 5) == 0
     assert lib.fa_bwd_workspace_size(B, N, 3, 2, d, 1, 0) == 0
     vf = lib.fa_varlen_fwd_workspace_size(5, 4000, Hq, Hkv, d, 1)
     vb = lib.fa_varlen_bwd_workspace_size(5, 4000, Hq, Hkv, d, 1, 1)
@@ -173,8 +179,9 @@ def test_varlen_rejects_bad_arguments(lib):
                              None) == WORKSPACE
     assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 0, 0, 2, 2, 64, 0.1, 1, 1, P, wb,
                              None) == INVALID
-    # the partial-sum dQ reduction is dense-only
+    # the partial-sum dQ reduction is dense-only; the fixed-point one is not
     assert lib.fa_varlen_bwd_workspace_size(3, 300, 2, 2, 64, 1, 2) == 0
+    assert lib.fa_varlen_bwd_workspace_size(3, 300, 2, 2, 64, 1, 4) > wb
     assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 2, P, wb,
                              None) == UNSUPPORTED
     assert lib.fa_varlen_bwd(P, P, P, P, P, P, P, P, P, P, 3, 300, 0, 2, 2, 64, 0.1, 1, 3, P, wb,
@@ -185,7 +192,7 @@ def test_varlen_qk_sizes_and_bad_arguments(lib):
     # equal lengths: the same workspace as the single-offset calls
     assert (lib.fa_varlen_qk_fwd_workspace_size(3, 300, 300, 2, 2, 64, 1)
             == lib.fa_varlen_fwd_workspace_size(3, 300, 2, 2, 64, 1))
-    for det in (0, 1):
+    for det in (0, 1, 4):
         assert (lib.fa_varlen_qk_bwd_workspace_size(3, 300, 300, 4, 2, 64, 1, det)
                 == lib.fa_varlen_bwd_workspace_size(3, 300, 4, 2, 64, 1, det))
     # the backward workspace grows with the query side (dQ accumulator, D, LSE)

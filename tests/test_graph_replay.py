@@ -1,6 +1,7 @@
 """The library's launches under HIP graph capture: the dense forward and the
-ordered (deterministic) backward, and the forward entry point that allocates
-nothing, are captured once and replayed several times, with eager work and
+deterministic backward (semaphore-ordered and fixed-point dQ, the latter with
+its K/V scan kernels), and the forward entry point that allocates nothing, are
+captured once and replayed several times, with eager work and
 synchronisations between the replays.  Every replay must reproduce the eager
 results bit for bit.  The library records no memset and no host
 synchronisation into the stream: the backward preprocess kernel clears the
@@ -38,16 +39,17 @@ def eager_noise(t):
     return float(y)
 
 
-def test_dense_forward_and_ordered_backward_replay(fa):
+@pytest.mark.parametrize("det", [1, 4], ids=["ordered", "fixed"])
+def test_dense_forward_and_deterministic_backward_replay(fa, det):
     import torch
     B, N, Hq, Hkv, d = 2, 300, 4, 2, 128
-    say(f"graph replay dense B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal, ordered dQ")
+    say(f"graph replay dense B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} causal, dQ mode {det}")
     x = inputs.dense_inputs(B, N, Hq, Hkv, d, seed=71)
     t = {n: to_dev(x[n]) for n in ("q", "k", "v", "do")}
     sc = scale_for(d)
     o0, lse0 = fa.fwd(t["q"], t["k"], t["v"], causal=True, softmax_scale=sc)
     g0 = fa.bwd(t["q"], t["k"], t["v"], o0, lse0, t["do"], causal=True, softmax_scale=sc,
-                deterministic=1)
+                deterministic=det)
     torch.cuda.synchronize()
 
     side = torch.cuda.Stream()  # default priority
@@ -56,7 +58,7 @@ def test_dense_forward_and_ordered_backward_replay(fa):
         for _ in range(2):
             o, lse = fa.fwd(t["q"], t["k"], t["v"], causal=True, softmax_scale=sc)
             fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=True, softmax_scale=sc,
-                   deterministic=1)
+                   deterministic=det)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
@@ -64,7 +66,7 @@ def test_dense_forward_and_ordered_backward_replay(fa):
     with torch.cuda.graph(graph):
         o, lse = fa.fwd(t["q"], t["k"], t["v"], causal=True, softmax_scale=sc)
         dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=True,
-                            softmax_scale=sc, deterministic=1)
+                            softmax_scale=sc, deterministic=det)
     for rep in range(4):
         eager_noise(t["q"])
         for buf in (o, lse, dq, dk, dv):

@@ -199,7 +199,8 @@ def headline(fa):
     return prob, refs
 
 
-@pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])
+@pytest.mark.parametrize("det", [0, 1, 2, 3, 4],
+                         ids=["atomic", "ordered", "partial", "fused", "fixed"])
 def test_headline_whole_heads(headline, det):
     prob, refs = headline
     grads = prob.backward(det)
@@ -209,7 +210,7 @@ def test_headline_whole_heads(headline, det):
     check_dk_sum(grads[1])
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3], ids=["ordered", "partial", "fused"])
+@pytest.mark.parametrize("mode", [1, 2, 3, 4], ids=["ordered", "partial", "fused", "fixed"])
 def test_headline_deterministic_bit_identical(headline, mode):
     import torch
     prob, _ = headline
@@ -236,7 +237,7 @@ def test_mha_2k(fa, d, causal):
 
 # ---- head dimension 256: B=2 H=8 N=4096 causal -------------------------------------
 
-@pytest.mark.parametrize("det", [0, 1], ids=["atomic", "ordered"])
+@pytest.mark.parametrize("det", [0, 1, 4], ids=["atomic", "ordered", "fixed"])
 def test_head_dim_256_whole_head(fa, det):
     prob = dense_problem(fa, 2, 4096, 8, 8, 256, True, seed=4)
     grads = prob.backward(det)
@@ -251,7 +252,8 @@ def test_head_dim_256_whole_head(fa, det):
 
 # ---- long context B=1 H=16 N=16384/32768 ----------------------------------------
 
-@pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])
+@pytest.mark.parametrize("det", [0, 1, 2, 3, 4],
+                         ids=["atomic", "ordered", "partial", "fused", "fixed"])
 @pytest.mark.parametrize("N", [16384, 32768])
 def test_long_context(fa, N, det):
     prob = dense_problem(fa, 1, N, 16, 16, 128, True, seed=2)
@@ -269,7 +271,8 @@ def test_long_context(fa, N, det):
 
 # ---- GQA / MQA B=2 Hq=32 Hkv=4/1 N=8192 ---------------------------------------------
 
-@pytest.mark.parametrize("det", [0, 1, 2, 3], ids=["atomic", "ordered", "partial", "fused"])
+@pytest.mark.parametrize("det", [0, 1, 2, 3, 4],
+                         ids=["atomic", "ordered", "partial", "fused", "fixed"])
 @pytest.mark.parametrize("hkv", [4, 1])
 def test_gqa_mqa(fa, hkv, det):
     prob = dense_problem(fa, 2, 8192, 32, hkv, 128, True, seed=3)
@@ -301,7 +304,7 @@ def packed(fa):
     return x, t, cu, o, lse, sc
 
 
-@pytest.mark.parametrize("det", [False, True], ids=["atomic", "deterministic"])
+@pytest.mark.parametrize("det", [0, 1, 4], ids=["atomic", "deterministic", "fixed"])
 def test_packed_varlen(fa, packed, det):
     import torch
     x, t, cu, o, lse, sc = packed
@@ -341,18 +344,20 @@ def test_packed_varlen(fa, packed, det):
     assert worst["dv_sum"] <= TOL_DV_SUM and worst["dk_sum"] <= TOL_DK_SUM
 
 
-def test_packed_varlen_deterministic_bit_identical(fa, packed):
+@pytest.mark.parametrize("det", [1, 4], ids=["ordered", "fixed"])
+def test_packed_varlen_deterministic_bit_identical(fa, packed, det):
     """The ordered dQ reduction of the packed batch (its own work order from
-    the scheduler, shortest first within each sequence) gives the same bits
-    on 10 repeated calls, with no device-reported error."""
+    the scheduler, shortest first within each sequence), and the fixed-point
+    one, give the same bits on 10 repeated calls, with no device-reported
+    error."""
     import torch
     x, t, cu, o, lse, sc = packed
-    ws = fa.varlen_bwd_workspace(cu.numel() - 1, x["q"].shape[0], 16, 16, 128, True, True,
+    ws = fa.varlen_bwd_workspace(cu.numel() - 1, x["q"].shape[0], 16, 16, 128, True, det,
                                  "cuda")
 
     def run():
         g = fa.varlen_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], cu, causal=True,
-                          softmax_scale=sc, deterministic=True, workspace=ws)
+                          softmax_scale=sc, deterministic=det, workspace=ws)
         torch.cuda.synchronize()
         assert fa.workspace_error(ws) == 0
         return g
