@@ -948,9 +948,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* o, const bf16*
     // their range (Popoviciu), <= |dO| max|V|.  beta < 2^k, so the sums stay
     // below 2^29 steps of 2^(k - 29), with 4x headroom in int32 for the
     // rounding of P, D and dS.
-    const float beta = sqrtf(nrm) * kvb[h / G];
-    int ex = kDqFixedBits - __builtin_amdgcn_frexp_expf(beta);
-    if (!(beta <= 3.0e38f)) ex = kDqExpNonFinite;
+    const int ex = dq_fixed_exponent(sqrtf(nrm) * kvb[h / G]);
     if (sub == 0) dq_exp[row] = ex;
   }
   if (dq_acc) {

@@ -43,6 +43,17 @@ constexpr int kDqFixedBits = 29;
 constexpr int kDqExpNonFinite = 1 << 20;
 constexpr int kKvBoundRows = 256;  // key rows per partial of the K/V magnitude scan
 
+// e for a row whose bound is beta: beta < 2^k (frexp), e = kDqFixedBits - k,
+// so every |x| <= beta has |x| 2^e < 2^kDqFixedBits, and 2^e is the largest
+// power of two that guarantees it (beta 2^e >= 2^(kDqFixedBits - 1)); beta = 0
+// gives kDqFixedBits, a non-finite beta kDqExpNonFinite.
+__host__ __device__ inline int dq_fixed_exponent(float beta) {
+  if (!(beta <= 3.40282347e38f)) return kDqExpNonFinite;
+  int k = 0;
+  (void)frexpf(beta, &k);
+  return kDqFixedBits - k;
+}
+
 // Index of the partial dQ tile of (query tile i, key tile j) inside its
 // (sequence, head): the query tiles' key-tile counts laid end to end (causal:
 // query tile i meets key tiles 0 .. i / (kBwdBC / kBwdBQ)).
