@@ -3,8 +3,9 @@
 One step = one forward and one backward pass over one batch of the headline
 workload (B=2, H=16, N=8192, d=128, bf16, causal), with seeded synthetic
 inputs already resident in HBM.  The backward reduces dQ across key tiles with
-int32 fixed-point atomic adds by default (--dq-mode 4: the fastest of the
-modes here, and bit-reproducible); --dq-mode 0 selects fp32 atomics.  Throughput counts the
+fp32 atomic adds (--dq-mode 0, the default); --dq-mode 4 selects the int32
+fixed-point adds, faster and bit-reproducible, whose resolution is set by a
+per-head bound of the inputs (see include/fa.h).  Throughput counts the
 algorithmic FLOPs 4*B*H*N^2*d/2 (forward) + 2.5x that (backward).
 
 With --workload decode the step is instead one forward and one backward over
@@ -641,7 +642,7 @@ def main():
     ap.add_argument("--Hkv", type=int, default=0)
     ap.add_argument("--d", type=int, default=128)
     ap.add_argument("--non-causal", action="store_true")
-    ap.add_argument("--dq-mode", type=int, default=4, choices=(0, 1, 2, 3, 4),
+    ap.add_argument("--dq-mode", type=int, default=0, choices=(0, 1, 2, 3, 4),
                     help="dQ reduction: 0 fp32 atomics, 1 semaphore-ordered, 2 partial tiles "
                          "summed by a second kernel, 3 partial tiles summed by the last "
                          "contributor, 4 int32 fixed-point atomics")

@@ -172,6 +172,11 @@ size_t fa_bwd_workspace_size(int B, int N, int Hq, int Hkv, int d, int causal,
  * key tiles) / 2 + 32 steps of 2^-e per element before the final bf16
  * rounding (a row's dQ has about 29 significant bits relative to its bound);
  * a row whose bound is not finite (non-finite dO, K or V) gets dQ = NaN.
+ * The step follows the bound, not the row's own dQ: one K or V row far
+ * larger than the rest of its head (an outlier in any sequence) coarsens the
+ * step of every row of that head by the same factor, which fp32 sums do not
+ * suffer; with 100x outliers the step nears the bf16 rounding of dQ, so
+ * modes 0 and 1 suit inputs with heavy-tailed K or V.
  * This is an MI355X-specific choice: int32 device atomics sustain about 1.7
  * TB/s against 1.35 TB/s for fp32 ones (fa_probe_dq_reduction).
  * Modes 1 to 4 make dQ/dK/dV bit-identical from run to run (and the
